@@ -1,0 +1,304 @@
+"""fp64 CPU oracle of the PACK3D local-global attention forward.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously correct
+statement of what the operator computes.  Only ``tests/``, the smoke check in
+``__graft_entry__.py`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+or call it.  The product path (``libpack3d`` and its Python binding) never
+does, and the two share no code: the only common module is ``synthgen``,
+which draws seeded inputs and holds none of the operator's arithmetic.
+
+Source: "Geometry Matters in Packed 3D Attention" (arXiv 2610.38694), as
+described on the papernotes.org notes page (method section, key designs 1-3
+and the flowchart) and restated on the ai.info summary page ("Methodology in
+Plain English").  Every function below cites the passage it follows.
+
+Everything is evaluated in float64 with numpy; inputs that were bf16 values
+are taken exactly (their float32 carriers upcast).
+
+Readings taken where the pages leave a step open (each is a parameter or a
+single constant; the full list with reasons is kept with the design notes):
+
+* frequencies: omega_{a,r} = base ** (-r / m_a) for r = 0..m_a-1 on each axis
+  a in (z, y, x); the pages fix only base 10 000 and m = (11, 11, 10).
+  PARITY UNPINNED for this choice: every identity the pages state holds for
+  any frequencies, so no pin below can tell two frequency rules apart.
+* pairs: rotation pair p acts on dims (2p, 2p+1), z pairs first, then y,
+  then x, as the block-diagonal direct sum is printed; dims past 2*sum(m)
+  are left alone (the identity block).
+* sign: each 2x2 block is [[cos, -sin], [sin, cos]] applied as R(c) x.
+* coordinates: integer lattice indices (z, y, x), origin 0.
+* softmax scale tau = 1/sqrt(d_h) in both branches unless given.
+* window: per-axis box |dz|<=wz//2, |dy|<=wy//2, |dx|<=wx//2, clipped at the
+  lattice faces, the query itself included.
+* summaries: aligned blocks, block index in block-raster order; every query
+  attends to all M summaries (its own block included); weights a are given
+  per token and KV group, uniform 1/v when absent.
+* KV groups: query head h reads KV group h // (Hq / Hkv).
+* gate: one 2-way softmax per token (index 0 = local, 1 = compressed), or
+  one per token and head when logits are [N, Hq, 2].
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "axial_frequencies", "rotation_matrix", "rotate", "block_index",
+    "block_summaries", "local_attention", "global_attention", "gate_weights",
+    "gate_mix", "forward", "local_window_sizes",
+]
+
+
+# ----------------------------------------------------------------------------
+# Axial grid RoPE  (papernotes.org notes, key design 1, the equation for R(c))
+# ----------------------------------------------------------------------------
+
+def axial_frequencies(rope_pairs: Sequence[int] = (11, 11, 10),
+                      base: float = 10000.0) -> list:
+    """Per-axis rotary frequencies omega_{a,r} = base^(-r/m_a), r < m_a."""
+    return [base ** (-np.arange(m, dtype=np.float64) / m) for m in rope_pairs]
+
+
+def rotation_matrix(c: Sequence[int], head_dim: int = 64,
+                    rope_pairs: Sequence[int] = (11, 11, 10),
+                    base: float = 10000.0) -> np.ndarray:
+    """The d_h x d_h matrix R(c): a direct sum over axes z, y, x and r < m_a of
+    2x2 rotations by omega_{a,r} * c_a, followed by an identity block."""
+    if 2 * sum(rope_pairs) > head_dim:
+        raise ValueError("rotary pairs exceed the head dimension")
+    omega = axial_frequencies(rope_pairs, base)
+    R = np.eye(head_dim)
+    p = 0
+    for a, m in enumerate(rope_pairs):
+        for r in range(m):
+            th = omega[a][r] * float(c[a])
+            R[2 * p:2 * p + 2, 2 * p:2 * p + 2] = [[math.cos(th), -math.sin(th)],
+                                                   [math.sin(th), math.cos(th)]]
+            p += 1
+    return R
+
+
+def rotate(x: np.ndarray, coords: np.ndarray,
+           rope_pairs: Sequence[int] = (11, 11, 10),
+           base: float = 10000.0) -> np.ndarray:
+    """R(c_i) x_{i,h} for every token i and head h.
+
+    ``x`` is ``[N, H, D]``; ``coords`` is integer ``[N, 3]`` (z, y, x).  The
+    same 2x2 blocks as :func:`rotation_matrix`, applied pair by pair.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = x.copy()
+    omega = axial_frequencies(rope_pairs, base)
+    p = 0
+    for a, m in enumerate(rope_pairs):
+        ca = np.asarray(coords[:, a], dtype=np.float64)
+        for r in range(m):
+            th = omega[a][r] * ca
+            cs, sn = np.cos(th)[:, None], np.sin(th)[:, None]
+            x0, x1 = x[:, :, 2 * p], x[:, :, 2 * p + 1]
+            y[:, :, 2 * p] = cs * x0 - sn * x1
+            y[:, :, 2 * p + 1] = sn * x0 + cs * x1
+            p += 1
+    return y
+
+
+# ----------------------------------------------------------------------------
+# Rotate-before-compression block summaries (papernotes.org notes, key
+# design 2, the equations for k~_j and v~_j; blocks are contiguous 3D boxes of
+# volume v, M = N / v)
+# ----------------------------------------------------------------------------
+
+def block_index(coords: np.ndarray, grid: Sequence[int], block: Sequence[int]) -> np.ndarray:
+    """Index j of the aligned block holding each cell, blocks in raster order."""
+    nby, nbx = grid[1] // block[1], grid[2] // block[2]
+    c = np.asarray(coords, dtype=np.int64)
+    return ((c[:, 0] // block[0]) * nby + c[:, 1] // block[1]) * nbx + c[:, 2] // block[2]
+
+
+def block_summaries(k_cmp: np.ndarray, v_cmp: np.ndarray, a: Optional[np.ndarray],
+                    coords: np.ndarray, grid: Sequence[int], block: Sequence[int],
+                    rope_pairs: Sequence[int] = (11, 11, 10), base: float = 10000.0,
+                    rope_coords: Optional[np.ndarray] = None):
+    """k~_j = sum_{u in B_j} a_u R(c_u) k_u and v~_j = sum_{u in B_j} a_u v_u.
+
+    ``k_cmp``/``v_cmp`` are ``[N, Hkv, D]`` (K unrotated: the rotation happens
+    here, before the weighted sum); ``a`` is ``[N, Hkv]`` or ``None`` for
+    uniform ``1/v``.  ``rope_coords`` replaces the coordinates used by the
+    rotation only (block membership still follows ``coords``).
+    Returns ``(k_sum, v_sum)``, each ``[Hkv, M, D]`` float64.
+    """
+    grid, block = tuple(grid), tuple(block)
+    if any(g % b for g, b in zip(grid, block)):
+        raise ValueError("block must divide the grid")
+    n, hkv, d = k_cmp.shape
+    vol = int(np.prod(block))
+    m = n // vol
+    kr = rotate(k_cmp, coords if rope_coords is None else rope_coords, rope_pairs, base)
+    w = (np.full((n, hkv), 1.0 / vol) if a is None else np.asarray(a, dtype=np.float64))
+    j = block_index(coords, grid, block)
+    cell = (np.asarray(coords[:, 0], np.int64) * grid[1] + coords[:, 1]) * grid[2] + coords[:, 2]
+    # group the members of each block together, raster order inside the block
+    srt = np.lexsort((cell, j))
+    wk = (w[:, :, None] * kr)[srt].reshape(m, vol, hkv, d).sum(axis=1)
+    wv = (w[:, :, None] * np.asarray(v_cmp, np.float64))[srt].reshape(m, vol, hkv, d).sum(axis=1)
+    return np.ascontiguousarray(wk.transpose(1, 0, 2)), np.ascontiguousarray(wv.transpose(1, 0, 2))
+
+
+# ----------------------------------------------------------------------------
+# Exact local-neighbourhood attention (papernotes.org notes, key design 3: the
+# neighbourhood N(i) is defined by lattice coordinates; ai.info summary,
+# Methodology in Plain English, the first of the three contracts)
+# ----------------------------------------------------------------------------
+
+def _window_offsets(window: Sequence[int]):
+    rz, ry, rx = (w // 2 for w in window)
+    return [(dz, dy, dx) for dz in range(-rz, rz + 1) for dy in range(-ry, ry + 1)
+            for dx in range(-rx, rx + 1)]
+
+
+def local_window_sizes(coords: np.ndarray, grid: Sequence[int], window: Sequence[int]) -> np.ndarray:
+    """|N(i)| for each token: the clipped box size."""
+    c = np.asarray(coords, np.int64)
+    size = np.ones(len(c), dtype=np.int64)
+    for a in range(3):
+        r = window[a] // 2
+        lo = np.maximum(c[:, a] - r, 0)
+        hi = np.minimum(c[:, a] + r, grid[a] - 1)
+        size *= hi - lo + 1
+    return size
+
+
+def local_attention(q_rot: np.ndarray, k_rot: np.ndarray, v: np.ndarray,
+                    coords: np.ndarray, grid: Sequence[int], window: Sequence[int],
+                    scale: float, rows: Optional[np.ndarray] = None, chunk: int = 8192):
+    """o_loc[i,h] = sum_{u in N(i)} softmax_u(scale * <q_i,h, k_u,g>) v_u,g.
+
+    Inputs are already rotated.  ``rows`` selects the query tokens computed
+    (default: all).  Returns ``(o_loc [R, Hq, D], lse [R, Hq])`` where ``lse``
+    is the natural-log log-sum-exp of the scaled logits.
+    """
+    grid = tuple(int(g) for g in grid)
+    if any(w % 2 == 0 for w in window):
+        raise ValueError("window extents must be odd")
+    n, hq, d = q_rot.shape
+    hkv = k_rot.shape[1]
+    grp = hq // hkv
+    coords = np.asarray(coords, np.int64)
+    lattice = np.full(grid, -1, dtype=np.int64)
+    lattice[coords[:, 0], coords[:, 1], coords[:, 2]] = np.arange(n)
+    offs = np.array(_window_offsets(window), dtype=np.int64)
+    rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
+    out = np.zeros((len(rows), hq, d))
+    lse = np.zeros((len(rows), hq))
+    gmax = np.array(grid, dtype=np.int64) - 1
+    for s in range(0, len(rows), chunk):
+        r = rows[s:s + chunk]
+        nr = len(r)
+        qc = np.asarray(q_rot[r], np.float64).reshape(nr, hkv, grp, d)
+        ci = coords[r]
+        logit = np.full((nr, len(offs), hkv, grp), -np.inf)
+        pos = np.zeros((nr, len(offs)), dtype=np.int64)
+        valid = np.zeros((nr, len(offs)), dtype=bool)
+        for t, off in enumerate(offs):
+            cu = ci + off
+            ok = np.all((cu >= 0) & (cu <= gmax), axis=1)
+            cc = np.clip(cu, 0, gmax)
+            pu = lattice[cc[:, 0], cc[:, 1], cc[:, 2]]
+            ku = np.asarray(k_rot[pu], np.float64)               # [nr, hkv, d]
+            lg = scale * np.einsum("nkgd,nkd->nkg", qc, ku)
+            logit[:, t] = np.where(ok[:, None, None], lg, -np.inf)
+            pos[:, t], valid[:, t] = pu, ok
+        mx = logit.max(axis=1, keepdims=True)
+        p = np.exp(logit - mx)
+        l = p.sum(axis=1)                                         # [nr, hkv, grp]
+        acc = np.zeros((nr, hkv, grp, d))
+        for t in range(len(offs)):
+            vu = np.asarray(v[pos[:, t]], np.float64) * valid[:, t, None, None]
+            acc += p[:, t, :, :, None] * vu[:, :, None, :]
+        out[s:s + nr] = (acc / l[..., None]).reshape(nr, hq, d)
+        lse[s:s + nr] = (mx[:, 0] + np.log(l)).reshape(nr, hq)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# Query -> all-summaries attention (papernotes.org notes, key design 3: each
+# query attends to the M summaries with a softmax; ai.info summary,
+# Methodology in Plain English, the second contract: all M summaries)
+# ----------------------------------------------------------------------------
+
+def global_attention(q_rot: np.ndarray, k_sum: np.ndarray, v_sum: np.ndarray,
+                     scale: float, rows: Optional[np.ndarray] = None):
+    """o_cmp[i,h] = sum_{j<M} softmax_j(scale * <q_i,h, k~_j,g>) v~_j,g.
+
+    ``q_rot`` is ``[N, Hq, D]``; ``k_sum``/``v_sum`` are ``[Hkv, M, D]``.
+    Returns ``(o_cmp [R, Hq, D], lse [R, Hq])`` (natural-log log-sum-exp).
+    """
+    n, hq, d = q_rot.shape
+    hkv, m, _ = k_sum.shape
+    grp = hq // hkv
+    rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
+    out = np.zeros((len(rows), hq, d))
+    lse = np.zeros((len(rows), hq))
+    chunk = max(1, (1 << 24) // (grp * m))
+    for s in range(0, len(rows), chunk):
+        r = rows[s:s + chunk]
+        for g in range(hkv):
+            qg = np.asarray(q_rot[r, g * grp:(g + 1) * grp], np.float64).reshape(-1, d)
+            t = scale * (qg @ np.asarray(k_sum[g], np.float64).T)     # [R*grp, M]
+            mx = t.max(axis=1, keepdims=True)
+            e = np.exp(t - mx)
+            l = e.sum(axis=1, keepdims=True)
+            o = (e @ np.asarray(v_sum[g], np.float64)) / l
+            out[s:s + len(r), g * grp:(g + 1) * grp] = o.reshape(len(r), grp, d)
+            lse[s:s + len(r), g * grp:(g + 1) * grp] = (mx + np.log(l)).reshape(len(r), grp)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# Tokenwise softmax gate (papernotes.org notes, flowchart node F and the
+# overall framework; ai.info summary: a learned tokenwise softmax mixer)
+# ----------------------------------------------------------------------------
+
+def gate_weights(gate_logits: np.ndarray) -> np.ndarray:
+    """(g_loc, g_cmp) = softmax over the last axis of size 2."""
+    lg = np.asarray(gate_logits, np.float64)
+    e = np.exp(lg - lg.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def gate_mix(o_loc: np.ndarray, o_cmp: np.ndarray, gate_logits: np.ndarray) -> np.ndarray:
+    """O = g_loc * o_loc + g_cmp * o_cmp with logits ``[N, 2]`` or ``[N, Hq, 2]``."""
+    g = gate_weights(gate_logits)
+    if g.ndim == 2:
+        g = g[:, None, :]
+    return g[..., 0:1] * o_loc + g[..., 1:2] * o_cmp
+
+
+# ----------------------------------------------------------------------------
+# The whole forward, in the flowchart's order (papernotes.org notes, overall
+# framework flowchart: RoPE, then the two branches, then the gate)
+# ----------------------------------------------------------------------------
+
+def forward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits,
+            rows: Optional[np.ndarray] = None, scale: Optional[float] = None) -> dict:
+    """Run the five steps and return the output and every intermediate.
+
+    ``p`` carries ``grid``, ``window``, ``block``, ``rope_pairs``,
+    ``rope_base`` and ``head_dim``.  Arrays are in packed order.  With
+    ``rows`` only those query tokens are computed (summaries are always
+    built in full).
+    """
+    tau = 1.0 / math.sqrt(p.head_dim) if scale is None else scale
+    q_rot = rotate(q, coords, p.rope_pairs, p.rope_base)
+    k_rot = rotate(k_loc, coords, p.rope_pairs, p.rope_base)
+    k_sum, v_sum = block_summaries(k_cmp, v_cmp, a, coords, p.grid, p.block,
+                                   p.rope_pairs, p.rope_base)
+    o_loc, lse_loc = local_attention(q_rot, k_rot, v_loc, coords, p.grid, p.window, tau, rows)
+    o_cmp, lse_cmp = global_attention(q_rot, k_sum, v_sum, tau, rows)
+    g = gate_logits if rows is None else np.asarray(gate_logits)[rows]
+    out = gate_mix(o_loc, o_cmp, g)
+    return dict(out=out, o_loc=o_loc, o_cmp=o_cmp, lse_loc=lse_loc, lse_cmp=lse_cmp,
+                k_sum=k_sum, v_sum=v_sum, q_rot=q_rot, k_rot=k_rot)
