@@ -1,0 +1,279 @@
+#!/usr/bin/env python
+"""Benchmark of the PACK3D local-global attention forward on one MI355X.
+
+One step = one ``pack3d_forward`` over the whole synthetic workload (RoPE on
+Q and K_loc, block summaries, local attention, query->summary attention with
+the fused gate), inputs resident in HBM.  Prints ONE JSON line with the
+throughput in tokens/s, the roofline position of the dominant kernel
+(k_global_attn, bf16 MFMA), per-kernel figures, and the fp64 CPU oracle timed
+on a bounded sample of the same workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--dense]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthgen as sg  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
+METRIC = "PACK3D attention fwd tokens/sec at 262k tokens; % bf16 MFMA peak; HBM GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_global_attn_block_bf16_64x64x64_hbm_traffic.txt")
+GLOBAL_SOURCES = [os.path.join(ROOT, "geometry_aware_local_amd", "csrc", f)
+                  for f in ("global_attn.hip", "pack3d_device.h")]
+
+
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per k_global_attn launch from the committed counter summary,
+    or None if it is missing or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    sha = re.search(r"^source_sha256_16:\s*(\w+)", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([\d.eE+]+)", text, re.M)
+    if not sha or not val or sha.group(1) != source_sha(GLOBAL_SOURCES):
+        return None
+    return float(val.group(1))
+
+
+def algorithmic(w: sg.Workload) -> dict:
+    """Work each step must do, per kernel (what the method moves or computes)."""
+    import oracle.pack3d_oracle as orc  # window counts only (closed form)
+    n, hq, hkv, m = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.n_blocks
+    es = 2 if w.dtype == "bf16" else 4
+    nbr = int(orc.local_window_sizes(sg.lattice_cells(w.grid), w.grid, w.window).sum())
+    return {
+        # rope: read + write Q and K_loc, read coords (twice: one launch each)
+        "rope_bytes": 2 * n * (hq + hkv) * 64 * es + 2 * n * 12,
+        # summary: read K_cmp, V_cmp, a, cell_to_pos; write K~, V~
+        "summary_bytes": 2 * n * hkv * 64 * es + n * hkv * 4 + n * 4 + 2 * hkv * m * 64 * es,
+        # local: QK^T and PV over every clipped window
+        "local_flops": 4 * nbr * hq * 64,
+        # global: QK^T and PV against all M summaries: 256 flops per (row, summary)
+        "global_flops": 4 * n * hq * m * 64,
+    }
+
+
+def cpu_baseline(w: sg.Workload, inp: sg.Inputs, rows: int) -> dict:
+    """The fp64 oracle on a bounded sample: rotated keys and summaries in full,
+    both branches and the gate for `rows` sampled query tokens; the whole-job
+    time is extrapolated linearly in the number of query tokens."""
+    import threadpoolctl
+    from oracle import pack3d_oracle as orc
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    sel = np.sort(np.random.default_rng(0).choice(w.n_tokens, rows, replace=False))
+    t0 = time.perf_counter()
+    k_rot = orc.rotate(inp.k_loc, inp.coords, w.rope_pairs, w.rope_base)
+    ks, vs = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block,
+                                 w.rope_pairs, w.rope_base)
+    t1 = time.perf_counter()
+    q_rot = orc.rotate(inp.q[sel], inp.coords[sel], w.rope_pairs, w.rope_base)
+    ol, _ = orc.local_attention(q_rot, k_rot, inp.v_loc, inp.coords, w.grid, w.window, 0.125,
+                                sel, q_is_rows=True)
+    oc, _ = orc.global_attention(q_rot, ks, vs, 0.125, q_is_rows=True)
+    orc.gate_mix(ol, oc, inp.gate[sel])
+    t2 = time.perf_counter()
+    whole = (t1 - t0) + (t2 - t1) * w.n_tokens / rows
+    return {"value": w.n_tokens / whole, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} of {w.n_tokens} query tokens (all heads), rotated keys and "
+                      f"summaries in full; {t2 - t0:.1f} s measured, whole job extrapolated "
+                      f"linearly in query tokens to {whole:.0f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="block_bf16_64x64x64", choices=sorted(sg.WORKLOADS))
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense", action="store_true",
+                    help="also time dense axial-RoPE attention (1x1x1 blocks) on the same inputs")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="for counter runs: a known-size copy probe, then each kernel 3 times")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the operator's "
+              "multi-GPU sharding is a design note, not built", file=sys.stderr)
+        return 2
+
+    import torch
+    from geometry_aware_local_amd import pack3d as pk
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 1
+
+    w = sg.WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = sg.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda x, t=None: None if x is None else torch.from_numpy(x).to(t).cuda() if t else \
+        torch.from_numpy(x).cuda()
+    q, k_loc, v_loc = dev(inp.q, dt), dev(inp.k_loc, dt), dev(inp.v_loc, dt)
+    k_cmp, v_cmp = dev(inp.k_cmp, dt), dev(inp.v_cmp, dt)
+    a, coords, c2p, gate = dev(inp.a), dev(inp.coords), dev(inp.cell_to_pos), dev(inp.gate)
+    prob = pk.make_problem(w.grid, w.n_q_heads, w.n_kv_heads, w.window, w.block, dt,
+                           w.rope_pairs, w.rope_base)
+    ws = pk.alloc_workspace(prob, q.device)
+    out = torch.empty_like(q)
+    n = w.n_tokens
+
+    def forward():
+        pk.pack3d_forward(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, c2p, gate,
+                          workspace=ws, out=out)
+
+    # split-op buffers (the same kernels the forward launches)
+    q_rot, k_rot = torch.empty_like(q), torch.empty_like(k_loc)
+
+    def split_ops():
+        return {
+            "k_rope": lambda: pk.pack3d_rope(prob, q, coords, out=q_rot),
+            "k_block_summary": lambda: pk.pack3d_block_summary(prob, k_cmp, v_cmp, a, c2p),
+            "k_local_attn": lambda: pk.pack3d_local_attn(prob, q_rot, k_rot, v_loc, c2p),
+            "k_global_attn": lambda: pk.pack3d_global_attn(prob, q_rot, ks, vs),
+        }
+
+    pk.pack3d_rope(prob, k_loc, coords, out=k_rot)
+    ks, vs = pk.pack3d_block_summary(prob, k_cmp, v_cmp, a, c2p)
+
+    if args.profile_only:
+        x = torch.empty(64 << 20, dtype=torch.float32, device="cuda")    # 256 MiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)           # copy probe: reads and writes 256 MiB
+        ops = split_ops()
+        for name in ("k_rope", "k_block_summary", "k_local_attn", "k_global_attn"):
+            for _ in range(3):
+                ops[name]()
+        forward()
+        torch.cuda.synchronize()
+        print("[bench] profile-only run done", file=sys.stderr, flush=True)
+        return 0
+
+    for _ in range(args.warmup):
+        forward()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        forward()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] forward {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    # per-kernel times: each split op launched back to back, HIP events on the
+    # current stream (the stream the binding launches on)
+    kern = {}
+    for name, fn in split_ops().items():
+        fn()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(args.kernel_reps):
+            fn()
+        b1.record()
+        torch.cuda.synchronize()
+        kern[name] = b0.elapsed_time(b1) / args.kernel_reps
+    work = algorithmic(w)
+    peak_mfma = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    g_tflops = work["global_flops"] / (kern["k_global_attn"] * 1e-3) / 1e12
+    es = 2 if w.dtype == "bf16" else 4
+    rope_q_bytes = 2 * n * w.n_q_heads * 64 * es + n * 12     # the timed op rotates Q only
+    kernels = {
+        "k_rope": {"ms": kern["k_rope"], "bound": "hbm",
+                   "gbs": rope_q_bytes / (kern["k_rope"] * 1e-3) / 1e9},
+        "k_block_summary": {"ms": kern["k_block_summary"], "bound": "hbm",
+                            "gbs": work["summary_bytes"] / (kern["k_block_summary"] * 1e-3) / 1e9},
+        "k_local_attn": {"ms": kern["k_local_attn"], "bound": "mfma",
+                         "tflops": work["local_flops"] / (kern["k_local_attn"] * 1e-3) / 1e12},
+        "k_global_attn": {"ms": kern["k_global_attn"], "bound": "mfma", "tflops": g_tflops},
+    }
+    for v in kernels.values():
+        if v["bound"] == "hbm":
+            v["frac"] = v["gbs"] / HBM_PEAK_GBS
+        else:
+            v["frac"] = v["tflops"] / peak_mfma
+
+    extra = {}
+    if args.dense:
+        dprob = pk.make_problem(w.grid, w.n_q_heads, w.n_kv_heads, w.window, (1, 1, 1), dt,
+                                w.rope_pairs, w.rope_base)
+        dk, dv = pk.pack3d_block_summary(dprob, k_cmp, v_cmp, None, c2p)
+        pk.pack3d_global_attn(dprob, q_rot, dk, dv)
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        pk.pack3d_global_attn(dprob, q_rot, dk, dv)
+        b1.record()
+        torch.cuda.synchronize()
+        dms = b0.elapsed_time(b1)
+        dfl = 4 * n * w.n_q_heads * n * 64
+        extra["dense_companion"] = {
+            "ms": dms, "tflops": dfl / (dms * 1e-3) / 1e12,
+            "frac": dfl / (dms * 1e-3) / 1e12 / peak_mfma,
+            "speedup_pack3d_vs_dense": dms / ms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp, min(args.cpu_rows, n))
+
+    line = {
+        "metric": METRIC,
+        "value": n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "grid": list(w.grid), "tokens": n, "packing": w.packing,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 64,
+                   "window": list(w.window), "block": list(w.block), "summaries": w.n_blocks,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "k_global_attn",
+                     "achieved": g_tflops, "peak": peak_mfma, "unit": "TFLOP/s",
+                     "frac": g_tflops / peak_mfma, "traffic": measured_traffic()},
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,292 @@
+// libpack3d C ABI: argument validation, problem geometry, workspace layout
+// and the launch sequence of the forward.  No device memory is allocated and
+// no host synchronisation happens here.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "pack3d_internal.h"
+
+using namespace pack3d;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return PACK3D_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PACK3D_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// Validate a problem and derive its geometry.  Host only, reads no device data.
+int make_geom(const pack3d_problem* p, Geom* g) {
+  if (!p) return fail(PACK3D_ERR_NULL, "problem is NULL");
+  for (int a = 0; a < 3; ++a)
+    if (p->grid[a] < 1) return fail(PACK3D_ERR_SHAPE, "grid[%d] = %d must be >= 1", a, p->grid[a]);
+  const int64_t n = (int64_t)p->grid[0] * p->grid[1] * p->grid[2];
+  if (n >= ((int64_t)1 << 31))
+    return fail(PACK3D_ERR_SHAPE, "N = %lld tokens does not fit int32 positions", (long long)n);
+  if (p->head_dim != kHeadDim)
+    return fail(PACK3D_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", p->head_dim);
+  if (p->n_q_heads < 1 || p->n_kv_heads < 1)
+    return fail(PACK3D_ERR_SHAPE, "head counts must be >= 1 (Hq %d, Hkv %d)", p->n_q_heads,
+                p->n_kv_heads);
+  if (p->n_q_heads % p->n_kv_heads)
+    return fail(PACK3D_ERR_SHAPE, "Hq %d is not a multiple of Hkv %d", p->n_q_heads, p->n_kv_heads);
+  for (int a = 0; a < 3; ++a) {
+    if (p->window[a] < 1 || p->window[a] % 2 == 0)
+      return fail(PACK3D_ERR_SHAPE, "window[%d] = %d must be odd and >= 1", a, p->window[a]);
+  }
+  if (p->window[1] > 7 || p->window[2] > 7 || p->window[0] > 31)
+    return fail(PACK3D_ERR_UNSUPPORTED, "window %dx%dx%d unsupported (y, x <= 7; z <= 31)",
+                p->window[0], p->window[1], p->window[2]);
+  int vol = 1;
+  for (int a = 0; a < 3; ++a) {
+    if (p->block[a] < 1) return fail(PACK3D_ERR_SHAPE, "block[%d] = %d must be >= 1", a, p->block[a]);
+    if (p->grid[a] % p->block[a])
+      return fail(PACK3D_ERR_SHAPE, "block[%d] = %d does not divide grid[%d] = %d", a, p->block[a],
+                  a, p->grid[a]);
+    vol *= p->block[a];
+  }
+  if (vol > kMaxBlockVol)
+    return fail(PACK3D_ERR_UNSUPPORTED, "block volume %d unsupported (max %d)", vol, kMaxBlockVol);
+  int pairs = 0;
+  for (int a = 0; a < 3; ++a) {
+    if (p->rope_pairs[a] < 0) return fail(PACK3D_ERR_SHAPE, "rope_pairs[%d] < 0", a);
+    pairs += p->rope_pairs[a];
+  }
+  if (2 * pairs > p->head_dim)
+    return fail(PACK3D_ERR_SHAPE, "2 * sum(rope_pairs) = %d exceeds head_dim", 2 * pairs);
+  if (!(p->rope_base > 0.0) || !isfinite(p->rope_base))
+    return fail(PACK3D_ERR_SHAPE, "rope_base must be finite and > 0");
+  if (p->dtype != PACK3D_F32 && p->dtype != PACK3D_BF16)
+    return fail(PACK3D_ERR_UNSUPPORTED, "dtype %d unsupported", p->dtype);
+  if (p->gate_per_head != 0 && p->gate_per_head != 1)
+    return fail(PACK3D_ERR_SHAPE, "gate_per_head must be 0 or 1");
+  if (!isfinite(p->scale)) return fail(PACK3D_ERR_SHAPE, "scale is not finite");
+
+  g->Z = p->grid[0];
+  g->Y = p->grid[1];
+  g->X = p->grid[2];
+  g->N = n;
+  g->Hq = p->n_q_heads;
+  g->Hkv = p->n_kv_heads;
+  g->G = p->n_q_heads / p->n_kv_heads;
+  g->rz = p->window[0] / 2;
+  g->ry = p->window[1] / 2;
+  g->rx = p->window[2] / 2;
+  g->bz = p->block[0];
+  g->by = p->block[1];
+  g->bx = p->block[2];
+  g->bvol = vol;
+  g->M = n / vol;
+  g->scale = p->scale > 0.0f ? p->scale : (float)(1.0 / sqrt((double)p->head_dim));
+  g->bf16 = p->dtype == PACK3D_BF16;
+  g->gate_per_head = p->gate_per_head;
+  // rotary table: pair p = r-th pair of axis a, omega = base^(-r/m_a), stored
+  // in turns (omega / 2pi)
+  memset(&g->rope, 0, sizeof g->rope);
+  int q = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int r = 0; r < p->rope_pairs[a]; ++r, ++q) {
+      g->rope.axis[q] = a;
+      g->rope.nu[q] = pow(p->rope_base, -(double)r / (double)p->rope_pairs[a]) /
+                      (2.0 * 3.14159265358979323846);
+    }
+  g->rope.npairs = q;
+  return ok();
+}
+
+bool local_supported(const Geom& g) {
+  return g.G == 1 || g.G == 2 || g.G == 4 || g.G == 8 || g.G == 16;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t q_rot, k_rot, k_sum, v_sum, o_loc, total;
+};
+
+WsLayout ws_layout(const Geom& g) {
+  const size_t es = g.bf16 ? 2 : 4;
+  WsLayout w;
+  size_t off = 0;
+  w.q_rot = off;
+  off += align256((size_t)g.N * g.Hq * 64 * es);
+  w.k_rot = off;
+  off += align256((size_t)g.N * g.Hkv * 64 * es);
+  w.k_sum = off;
+  off += align256((size_t)g.Hkv * g.M * 64 * es);
+  w.v_sum = off;
+  off += align256((size_t)g.Hkv * g.M * 64 * es);
+  w.o_loc = off;
+  off += align256((size_t)g.N * g.Hq * 64 * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pack3d_version(void) { return PACK3D_VERSION; }
+
+const char* pack3d_last_error(void) { return g_err.c_str(); }
+
+const char* pack3d_backend_info(void) {
+  return "libpack3d gfx950: rope=k_rope (VALU, 16B rows); "
+         "block_summary=k_block_summary (wave per block, XOR-tree reduction); "
+         "local_attn=k_local_attn (LDS plane tiles + halo, masked-dense MFMA 32x32x16 bf16 / "
+         "32x32x2 f32); global_attn=k_global_attn (LDS double-buffered summary tiles, "
+         "MFMA 32x32x16 bf16 / 32x32x2 f32, online softmax, fused gate epilogue in forward); "
+         "gate_mix=k_gate_mix; no fallbacks";
+}
+
+size_t pack3d_forward_workspace_size(const pack3d_problem* prob) {
+  Geom g;
+  if (make_geom(prob, &g) != PACK3D_OK) return 0;
+  return ws_layout(g).total;
+}
+
+int pack3d_rope(const pack3d_problem* prob, const void* x, void* y, int32_t n_heads,
+                const int32_t* coords, void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!x || !y || !coords) return fail(PACK3D_ERR_NULL, "pack3d_rope: NULL tensor argument");
+  if (n_heads < 1) return fail(PACK3D_ERR_SHAPE, "pack3d_rope: n_heads = %d", n_heads);
+  return hip_status(launch_rope(g, x, y, n_heads, coords, (hipStream_t)stream), "k_rope");
+}
+
+int pack3d_block_summary(const pack3d_problem* prob, const void* k_cmp, const void* v_cmp,
+                         const float* a, const int32_t* cell_to_pos, void* k_sum, void* v_sum,
+                         void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!k_cmp || !v_cmp || !cell_to_pos || !k_sum || !v_sum)
+    return fail(PACK3D_ERR_NULL, "pack3d_block_summary: NULL tensor argument");
+  return hip_status(launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
+                                         (hipStream_t)stream),
+                    "k_block_summary");
+}
+
+int pack3d_local_attn(const pack3d_problem* prob, const void* q_rot, const void* k_rot,
+                      const void* v, const int32_t* cell_to_pos, float* o_loc, float* lse_loc,
+                      void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!q_rot || !k_rot || !v || !cell_to_pos || !o_loc)
+    return fail(PACK3D_ERR_NULL, "pack3d_local_attn: NULL tensor argument");
+  if (!local_supported(g))
+    return fail(PACK3D_ERR_UNSUPPORTED, "pack3d_local_attn: Hq/Hkv = %d unsupported", g.G);
+  return hip_status(
+      launch_local_attn(g, q_rot, k_rot, v, cell_to_pos, o_loc, lse_loc, (hipStream_t)stream),
+      "k_local_attn");
+}
+
+int pack3d_global_attn(const pack3d_problem* prob, const void* q_rot, const void* k_sum,
+                       const void* v_sum, int32_t m, float* o_cmp, float* lse_cmp,
+                       void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!q_rot || !k_sum || !v_sum || !o_cmp)
+    return fail(PACK3D_ERR_NULL, "pack3d_global_attn: NULL tensor argument");
+  if (m < 1) return fail(PACK3D_ERR_SHAPE, "pack3d_global_attn: m = %d must be >= 1", m);
+  return hip_status(launch_global_attn(g, q_rot, k_sum, v_sum, m, o_cmp, lse_cmp, nullptr,
+                                       nullptr, nullptr, (hipStream_t)stream),
+                    "k_global_attn");
+}
+
+int pack3d_gate_mix(const pack3d_problem* prob, const float* o_loc, const float* o_cmp,
+                    const float* gate_logits, void* out, void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!o_loc || !o_cmp || !gate_logits || !out)
+    return fail(PACK3D_ERR_NULL, "pack3d_gate_mix: NULL tensor argument");
+  return hip_status(launch_gate_mix(g, o_loc, o_cmp, gate_logits, out, (hipStream_t)stream),
+                    "k_gate_mix");
+}
+
+int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
+                   const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                   const int32_t* coords, const int32_t* cell_to_pos, const float* gate_logits,
+                   void* out, void* workspace, size_t ws_bytes, void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!q || !k_loc || !v_loc || !k_cmp || !v_cmp || !coords || !cell_to_pos || !gate_logits ||
+      !out)
+    return fail(PACK3D_ERR_NULL, "pack3d_forward: NULL tensor argument");
+  if (!local_supported(g))
+    return fail(PACK3D_ERR_UNSUPPORTED, "pack3d_forward: Hq/Hkv = %d unsupported", g.G);
+  const WsLayout w = ws_layout(g);
+  if (!workspace) return fail(PACK3D_ERR_WORKSPACE, "pack3d_forward: workspace is NULL");
+  if (ws_bytes < w.total)
+    return fail(PACK3D_ERR_WORKSPACE, "pack3d_forward: workspace %zu bytes < %zu needed", ws_bytes,
+                w.total);
+  if ((uintptr_t)workspace & 255)
+    return fail(PACK3D_ERR_WORKSPACE, "pack3d_forward: workspace not 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* q_rot = ws + w.q_rot;
+  void* k_rot = ws + w.k_rot;
+  void* k_sum = ws + w.k_sum;
+  void* v_sum = ws + w.v_sum;
+  float* o_loc = (float*)(ws + w.o_loc);
+  hipError_t e;
+  if ((e = launch_rope(g, q, q_rot, g.Hq, coords, s)) != hipSuccess) return hip_status(e, "k_rope(q)");
+  if ((e = launch_rope(g, k_loc, k_rot, g.Hkv, coords, s)) != hipSuccess)
+    return hip_status(e, "k_rope(k_loc)");
+  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum, s)) != hipSuccess)
+    return hip_status(e, "k_block_summary");
+  if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, nullptr, s)) != hipSuccess)
+    return hip_status(e, "k_local_attn");
+  e = launch_global_attn(g, q_rot, k_sum, v_sum, g.M, nullptr, nullptr, o_loc, gate_logits, out, s);
+  return hip_status(e, "k_global_attn(gated)");
+}
+
+int pack3d_build_cell_index(const pack3d_problem* prob, const int32_t* coords,
+                            int32_t* cell_to_pos, void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!coords || !cell_to_pos)
+    return fail(PACK3D_ERR_NULL, "pack3d_build_cell_index: NULL tensor argument");
+  return hip_status(launch_build_cell_index(g, coords, cell_to_pos, (hipStream_t)stream),
+                    "k_cell_index");
+}
+
+int pack3d_check_packing(const pack3d_problem* prob, const int32_t* coords,
+                         const int32_t* cell_to_pos, int32_t* n_bad_dev, void* stream) {
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!coords || !cell_to_pos || !n_bad_dev)
+    return fail(PACK3D_ERR_NULL, "pack3d_check_packing: NULL tensor argument");
+  return hip_status(launch_check_packing(g, coords, cell_to_pos, n_bad_dev, (hipStream_t)stream),
+                    "k_check_packing");
+}
+
+}  // extern "C"

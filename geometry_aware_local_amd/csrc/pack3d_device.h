@@ -1,0 +1,280 @@
+// Device-side helpers shared by the libpack3d kernels: element types, vector
+// loads, the rotary sine/cosine, and the gfx950 MFMA tile primitives used by
+// both attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "pack3d_internal.h"
+
+namespace pack3d {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v) { return (float)v; }
+template <typename T>
+__device__ __forceinline__ T from_f32(float v) { return (T)v; }
+
+// 16-byte vector load/store through plain (vector-memory) instructions.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// Rotary sine and cosine of 2*pi*nu*c.
+//
+// The angle is reduced in double to the nearest quarter turn, so the float
+// argument is |x| <= pi/4 whatever the coordinate; sin and cos of x are then
+// the Taylor series to x^9 and x^10 (truncation below 2e-9 on |x| <= pi/4),
+// and the quarter-turn index k selects and signs the pair.  Depends only on
+// (nu, c), so every kernel rotates a given cell identically.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rope_sincos(double nu, int c, float& sn, float& cs) {
+  const double t = nu * (double)c;                      // turns
+  const double q = rint(4.0 * t);                       // quarter turns
+  const float x = (float)((t - 0.25 * q) * 6.283185307179586);
+  const int k = ((int)q) & 3;
+  const float x2 = x * x;
+  const float s = x + x * x2 * (-1.0f / 6.0f + x2 * (1.0f / 120.0f +
+                  x2 * (-1.0f / 5040.0f + x2 * (1.0f / 362880.0f))));
+  const float c0 = 1.0f + x2 * (-0.5f + x2 * (1.0f / 24.0f + x2 * (-1.0f / 720.0f +
+                   x2 * (1.0f / 40320.0f + x2 * (-1.0f / 3628800.0f)))));
+  // sin(x + k pi/2), cos(x + k pi/2)
+  const float a = (k & 1) ? c0 : s;
+  const float b = (k & 1) ? s : c0;
+  sn = (k & 2) ? -a : a;
+  cs = ((k + 1) & 2) ? -b : b;
+}
+
+// Rotate 4 consecutive pairs (dims 8*chunk .. 8*chunk+7) held as floats.
+__device__ __forceinline__ void rotate8(float* v, const float* sn, const float* cs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = v[2 * i], x1 = v[2 * i + 1];
+    v[2 * i] = cs[i] * x0 - sn[i] * x1;
+    v[2 * i + 1] = sn[i] * x0 + cs[i] * x1;
+  }
+}
+
+// cos/sin for the 4 pairs of dim-chunk `chunk` (8 dims) at cell (z, y, x).
+__device__ __forceinline__ void chunk_sincos(const RopeTab& rt, int chunk, int z, int y, int x,
+                                             float* sn, float* cs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = chunk * 4 + i;
+    if (p < rt.npairs) {
+      const int ax = rt.axis[p];
+      const int c = ax == 0 ? z : (ax == 1 ? y : x);
+      rope_sincos(rt.nu[p], c, sn[i], cs[i]);
+    } else {
+      sn[i] = 0.0f;
+      cs[i] = 1.0f;
+    }
+  }
+}
+
+// Load / store 8 consecutive elements as floats.
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v) {
+  if constexpr (std::is_same<T, float>::value) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  } else {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float* v) {
+  if constexpr (std::is_same<T, float>::value) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[4 + i]; }
+    *reinterpret_cast<f32x4*>(p) = a;
+    *reinterpret_cast<f32x4*>(p + 4) = b;
+  } else {
+    bf16x8 a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (bf16_t)v[i];
+    *reinterpret_cast<bf16x8*>(p) = a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA tile primitives (gfx950, wave64).
+//
+// Both attention kernels compute S^T = K Q^T and O^T = V^T P^T with 32x32
+// output tiles: keys (or head dims) are MFMA rows, query rows are MFMA
+// columns.  Accumulator element v (0..15) of lane l holds row
+// 8*(v/4) + 4*(l/32) + (v%4) of column l%32.
+//
+// QK^T contraction over the 64 head dims: lane half h = l/32 supplies dims
+// h*32 .. h*32+31 of its key row (A) and of its query row (B), in the same
+// order, so any internal k ordering of the instruction is immaterial.
+//   bf16: 4 x v_mfma_f32_32x32x16_bf16, step s takes dims h*32 + 8s .. +7
+//   fp32: 32 x v_mfma_f32_32x32x2_f32,  step s takes dim  h*32 + s
+// PV contraction over 32 keys: the B operand is the lane's own accumulator
+// (the P^T column), so the A operand (V^T) must hold, for element e of step
+// t, the value of key kr(t, e, h) below.
+//   bf16: 2 steps x 8 elements;  fp32: 16 steps x 1 element.
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16_t> {
+  static constexpr int kQkSteps = 4;
+  static constexpr int kPvSteps = 2;
+  static constexpr int kPerStep = 8;
+  typedef bf16x8 frag;
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // key row (within the 32-key block) of PV step t, element e, lane half h
+  __device__ static __forceinline__ int kr(int t, int e, int h) {
+    return 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+  }
+  // B operand of PV step t from the accumulator (P^T column)
+  __device__ static __forceinline__ frag p_frag(const f32x16& p, int t) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16_t)p[8 * t + e];
+    return f;
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int kQkSteps = 32;
+  static constexpr int kPvSteps = 16;
+  static constexpr int kPerStep = 1;
+  typedef float frag;
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ int kr(int t, int e, int h) {
+    (void)e;
+    return 8 * (t >> 2) + 4 * h + (t & 3);
+  }
+  __device__ static __forceinline__ frag p_frag(const f32x16& p, int t) { return p[t]; }
+};
+
+// Query fragment: the lane's 32 dims (h*32 ..) of one query row, as the MFMA
+// B operand of every QK^T step.
+template <typename T>
+struct QFrag {
+  typename Mma<T>::frag f[Mma<T>::kQkSteps];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_qfrag(QFrag<T>& q, const T* row_h /* row + h*32 */,
+                                           bool valid) {
+  if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f32x4 v = valid ? *reinterpret_cast<const f32x4*>(row_h + 4 * i) : f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q.f[4 * i + j] = v[j];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 v;
+      if (valid) {
+        v = *reinterpret_cast<const bf16x8*>(row_h + 8 * s);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16_t)0.0f;
+      }
+      q.f[s] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layouts.
+//
+// K rows: [rows][64] elements with the 16-byte chunks of row r XOR-swizzled
+// by (r & 7), so the 32 rows read by one MFMA operand spread over all banks.
+// V^T: [64 dims][ld] elements, ld = key capacity + 4, so consecutive dims
+// start on different banks.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct KLds {
+  static constexpr int kChunkElems = 16 / sizeof(T);       // elements per 16 B
+  static constexpr int kChunks = 64 / kChunkElems;          // chunks per row
+  __device__ static __forceinline__ int chunk_off(int row, int chunk) {
+    return row * 64 + ((chunk ^ (row & 7)) * kChunkElems);
+  }
+};
+
+// A operand of QK^T step s for key row `row` (lane half h).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag k_frag(const T* ks, int row, int h, int s) {
+  if constexpr (std::is_same<T, float>::value) {
+    const int dim = h * 32 + s;
+    return ks[KLds<T>::chunk_off(row, dim >> 2) + (dim & 3)];
+  } else {
+    const int chunk = h * 4 + s;
+    return *reinterpret_cast<const bf16x8*>(ks + KLds<T>::chunk_off(row, chunk));
+  }
+}
+
+// Full K fragment set for one key row: all QK^T steps (fp32 reads 8 chunks).
+template <typename T>
+struct KFrag {
+  typename Mma<T>::frag f[Mma<T>::kQkSteps];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_kfrag(KFrag<T>& k, const T* ks, int row, int h) {
+  if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ks + KLds<T>::chunk_off(row, h * 8 + i));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k.f[4 * i + j] = v[j];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) k.f[s] = k_frag<T>(ks, row, h, s);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ f32x16 qk_tile(const KFrag<T>& k, const QFrag<T>& q) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < Mma<T>::kQkSteps; ++s) acc = Mma<T>::mma(k.f[s], q.f[s], acc);
+  return acc;
+}
+
+// Online-softmax state of one query column (per lane; lanes l and l+32 hold
+// the same column and always agree on m).
+struct SoftmaxState {
+  float m;   // running reference max, in scaled log2 units
+  float l;   // this lane's partial sum of exponentials
+};
+
+// Lazy rescaling: the reference max only moves when a tile's max exceeds it
+// by more than kRescaleSlack (log2 units), so exponentials stay below
+// 2^kRescaleSlack.  The decision is per column; skipping the O update when no
+// column moves changes no value (the factor would be exactly 1).
+constexpr float kRescaleSlack = 8.0f;
+
+}  // namespace pack3d

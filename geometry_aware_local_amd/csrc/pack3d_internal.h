@@ -1,0 +1,62 @@
+// Internal declarations shared by the libpack3d translation units: the
+// validated problem geometry, the rotary table and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pack3d.h"
+
+namespace pack3d {
+
+constexpr int kHeadDim = 64;
+constexpr int kMaxPairs = 32;      // head_dim / 2
+constexpr int kMaxBlockVol = 64;
+constexpr int kNumXcd = 8;         // MI355X: 8 XCDs, each with its own L2
+
+// Rotary constants: pair p rotates dims (2p, 2p+1) by 2*pi * nu[p] * c[axis[p]]
+// (nu = omega / 2pi, computed on the host in double).  Pairs >= npairs are
+// the identity block.
+struct RopeTab {
+  double nu[kMaxPairs];
+  int32_t axis[kMaxPairs];
+  int32_t npairs;
+};
+
+// Everything a kernel needs, derived once from pack3d_problem on the host.
+struct Geom {
+  int32_t Z, Y, X;
+  int64_t N;
+  int32_t Hq, Hkv, G;             // G = Hq / Hkv
+  int32_t rz, ry, rx;             // window radii
+  int32_t bz, by, bx, bvol;       // summary block
+  int64_t M;                      // N / bvol
+  float scale;                    // softmax scale
+  int32_t bf16;                   // 1: bf16 tensors, 0: fp32
+  int32_t gate_per_head;
+  RopeTab rope;
+};
+
+// Launchers (each returns the launch status; no host synchronisation).
+hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
+                       const int32_t* coords, hipStream_t s);
+hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_cmp,
+                                const float* a, const int32_t* cell_to_pos, void* k_sum,
+                                void* v_sum, hipStream_t s);
+hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot,
+                             const void* v, const int32_t* cell_to_pos, float* o_loc,
+                             float* lse, hipStream_t s);
+// o_cmp != nullptr: write o_cmp (fp32).  Otherwise gate-mix epilogue:
+// out = g_loc*o_loc + g_cmp*o_cmp in the problem dtype.
+hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
+                              const void* v_sum, int64_t m, float* o_cmp, float* lse,
+                              const float* o_loc, const float* gate, void* out,
+                              hipStream_t s);
+hipError_t launch_gate_mix(const Geom& g, const float* o_loc, const float* o_cmp,
+                           const float* gate, void* out, hipStream_t s);
+hipError_t launch_build_cell_index(const Geom& g, const int32_t* coords, int32_t* c2p,
+                                   hipStream_t s);
+hipError_t launch_check_packing(const Geom& g, const int32_t* coords, const int32_t* c2p,
+                                int32_t* n_bad, hipStream_t s);
+
+}  // namespace pack3d

@@ -1,0 +1,146 @@
+// Axial grid RoPE and the rotate-before-compression block summaries.
+//
+// "Geometry Matters in Packed 3D Attention", papernotes.org notes:
+//   key design 1 - R(c) is a direct sum over the axes z, y, x of 2x2
+//     rotations by omega_{a,r} * c_a, applied to queries and keys only;
+//   key design 2 - each block summary is the normalised weighted sum of the
+//     ROTATED keys of its cells (and of the unrotated values), so the
+//     query-summary logit keeps every cell's displacement from the query.
+//
+// Both kernels are HBM streams: lanes own 16-byte chunks (8 dims) of token
+// rows, so every wave moves whole 128-byte rows.
+#include "pack3d_device.h"
+
+namespace pack3d {
+
+// ---------------------------------------------------------------------------
+// k_rope: y[i, h, :] = R(coords[i]) x[i, h, :].
+// 8 lanes per token, lane c owns dims 8c..8c+7 (4 rotary pairs) of every head:
+// its 4 sines/cosines are computed once and reused for all heads.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope(const T* __restrict__ x, T* y, int64_t n,
+                                              int32_t heads, const int32_t* __restrict__ coords,
+                                              RopeTab rt) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tok = gid >> 3;
+  const int chunk = (int)(gid & 7);
+  if (tok >= n) return;
+  const int z = coords[3 * tok], yy = coords[3 * tok + 1], xx = coords[3 * tok + 2];
+  float sn[4], cs[4];
+  chunk_sincos(rt, chunk, z, yy, xx, sn, cs);
+  const T* src = x + tok * heads * 64 + chunk * 8;
+  T* dst = y + tok * heads * 64 + chunk * 8;
+  for (int h = 0; h < heads; ++h) {
+    float v[8];
+    load8<T>(src + h * 64, v);
+    rotate8(v, sn, cs);
+    store8<T>(dst + h * 64, v);
+  }
+}
+
+hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
+                       const int32_t* coords, hipStream_t s) {
+  const int64_t threads = g.N * 8;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (g.bf16)
+    hipLaunchKernelGGL(k_rope<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x, (bf16_t*)y,
+                       g.N, heads, coords, g.rope);
+  else
+    hipLaunchKernelGGL(k_rope<float>, grid, dim3(256), 0, s, (const float*)x, (float*)y, g.N,
+                       heads, coords, g.rope);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// k_block_summary: one wave per block j.
+// Lane = (cell slot u8 = lane/8, chunk = lane%8).  The block's cells are taken
+// in raster order, 8 per pass; each lane rotates its K chunk by its cell's
+// coordinates (rotation before the weighted sum), weights K and V by a, and
+// accumulates in fp32.  The 8 cell slots are then reduced with a fixed XOR
+// tree, so the summation order depends only on cell positions.
+// ---------------------------------------------------------------------------
+constexpr int kSumWaves = 4;
+constexpr int kMaxPasses = kMaxBlockVol / 8;
+
+template <typename T>
+__global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
+    const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ a,
+    const int32_t* __restrict__ c2p, T* __restrict__ ks, T* __restrict__ vs, Geom g) {
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * kSumWaves + (threadIdx.x >> 6);
+  if (j >= g.M) return;
+  const int slot = lane >> 3, chunk = lane & 7;
+  const int nbx = g.X / g.bx, nby = g.Y / g.by;
+  const int jx = (int)(j % nbx), jy = (int)((j / nbx) % nby), jz = (int)(j / ((int64_t)nbx * nby));
+  const int passes = (g.bvol + 7) >> 3;
+  const float uniform = 1.0f / (float)g.bvol;
+
+  // positions and rotations of the lane's cells (one per pass)
+  int64_t pos[kMaxPasses];
+  float sn[kMaxPasses][4], cs[kMaxPasses][4];
+#pragma unroll
+  for (int p = 0; p < kMaxPasses; ++p) {
+    pos[p] = -1;
+    if (p < passes) {
+      const int u = p * 8 + slot;
+      if (u < g.bvol) {
+        const int ux = u % g.bx, uy = (u / g.bx) % g.by, uz = u / (g.bx * g.by);
+        const int z = jz * g.bz + uz, y = jy * g.by + uy, x = jx * g.bx + ux;
+        pos[p] = c2p[((int64_t)z * g.Y + y) * g.X + x];
+        chunk_sincos(g.rope, chunk, z, y, x, sn[p], cs[p]);
+      }
+    }
+  }
+
+  for (int grp = 0; grp < g.Hkv; ++grp) {
+    float ak[8], av[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ak[i] = av[i] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kMaxPasses; ++p) {
+      if (p < passes && pos[p] >= 0) {
+        const int64_t row = (pos[p] * g.Hkv + grp) * 64 + chunk * 8;
+        float kv[8], vv[8];
+        load8<T>(kc + row, kv);
+        load8<T>(vc + row, vv);
+        const float w = a ? a[pos[p] * g.Hkv + grp] : uniform;
+        rotate8(kv, sn[p], cs[p]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ak[i] += w * kv[i];
+          av[i] += w * vv[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ak[i] += __shfl_xor(ak[i], off);
+        av[i] += __shfl_xor(av[i], off);
+      }
+    }
+    if (slot == 0) {
+      const int64_t o = ((int64_t)grp * g.M + j) * 64 + chunk * 8;
+      store8<T>(ks + o, ak);
+      store8<T>(vs + o, av);
+    }
+  }
+}
+
+hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_cmp,
+                                const float* a, const int32_t* c2p, void* k_sum, void* v_sum,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)((g.M + kSumWaves - 1) / kSumWaves));
+  const dim3 block(64 * kSumWaves);
+  if (g.bf16)
+    hipLaunchKernelGGL(k_block_summary<bf16_t>, grid, block, 0, s, (const bf16_t*)k_cmp,
+                       (const bf16_t*)v_cmp, a, c2p, (bf16_t*)k_sum, (bf16_t*)v_sum, g);
+  else
+    hipLaunchKernelGGL(k_block_summary<float>, grid, block, 0, s, (const float*)k_cmp,
+                       (const float*)v_cmp, a, c2p, (float*)k_sum, (float*)v_sum, g);
+  return hipGetLastError();
+}
+
+}  // namespace pack3d

@@ -1,0 +1,288 @@
+"""Python binding of libpack3d: the PACK3D local-global attention forward on MI355X.
+
+Argument marshalling only.  Every step of the operator runs in libpack3d's
+HIP kernels; PyTorch provides device memory and the current HIP stream.  The
+functions carry the names of the C entry points declared in
+``include/pack3d.h`` and take torch tensors in the layouts documented there:
+
+* ``q``            ``[N, Hq, 64]``  float32 or bfloat16, packed token order
+* ``k_*``, ``v_*`` ``[N, Hkv, 64]`` same dtype
+* ``a``            ``[N, Hkv]``     float32 summary weights, or ``None`` (uniform)
+* ``coords``       ``[N, 3]``       int32 (z, y, x)
+* ``cell_to_pos``  ``[Z*Y*X]``      int32
+* ``gate``         ``[N, 2]`` (or ``[N, Hq, 2]``) float32 logits, index 0 = local
+
+There is no fallback: importing this module fails if ``libpack3d.so`` has not
+been built (``python -m geometry_aware_local_amd.build``), and every call
+raises :class:`Pack3DError` when the library rejects its arguments.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpack3d.so")
+
+PACK3D_F32, PACK3D_BF16 = 0, 1
+STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_UNSUPPORTED", -4: "ERR_WORKSPACE",
+          -5: "ERR_PACKING", -6: "ERR_HIP"}
+
+EXPORTS = (
+    "pack3d_rope", "pack3d_block_summary", "pack3d_local_attn", "pack3d_global_attn",
+    "pack3d_gate_mix", "pack3d_forward", "pack3d_forward_workspace_size",
+    "pack3d_build_cell_index", "pack3d_check_packing", "pack3d_last_error",
+    "pack3d_backend_info", "pack3d_version",
+)
+
+
+class Pack3DError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libpack3d {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``pack3d_problem``."""
+    _fields_ = [
+        ("grid", ctypes.c_int32 * 3),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32 * 3),
+        ("block", ctypes.c_int32 * 3),
+        ("rope_pairs", ctypes.c_int32 * 3),
+        ("rope_base", ctypes.c_double),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+        ("gate_per_head", ctypes.c_int32),
+    ]
+
+    @property
+    def n_tokens(self) -> int:
+        return self.grid[0] * self.grid[1] * self.grid[2]
+
+    @property
+    def n_blocks(self) -> int:
+        return self.n_tokens // (self.block[0] * self.block[1] * self.block[2])
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == PACK3D_BF16 else torch.float32
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m geometry_aware_local_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, V, I32, SZ = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "pack3d_rope": [P, V, V, I32, V, V],
+        "pack3d_block_summary": [P, V, V, V, V, V, V, V],
+        "pack3d_local_attn": [P, V, V, V, V, V, V, V],
+        "pack3d_global_attn": [P, V, V, V, I32, V, V, V],
+        "pack3d_gate_mix": [P, V, V, V, V, V],
+        "pack3d_forward": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V],
+        "pack3d_build_cell_index": [P, V, V, V],
+        "pack3d_check_packing": [P, V, V, V, V],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes, fn.restype = args, ctypes.c_int
+    lib.pack3d_forward_workspace_size.argtypes = [P]
+    lib.pack3d_forward_workspace_size.restype = ctypes.c_size_t
+    for name in ("pack3d_last_error", "pack3d_backend_info"):
+        getattr(lib, name).argtypes, getattr(lib, name).restype = [], ctypes.c_char_p
+    lib.pack3d_version.argtypes, lib.pack3d_version.restype = [], ctypes.c_int
+    return lib
+
+
+LIB = _load()
+
+
+def make_problem(grid: Sequence[int], n_q_heads: int, n_kv_heads: int,
+                 window: Sequence[int] = (3, 7, 7), block: Sequence[int] = (1, 4, 4),
+                 dtype: torch.dtype = torch.bfloat16, rope_pairs: Sequence[int] = (11, 11, 10),
+                 rope_base: float = 10000.0, scale: float = 0.0, head_dim: int = 64,
+                 gate_per_head: bool = False) -> Problem:
+    p = Problem()
+    p.grid[:] = list(grid)
+    p.n_q_heads, p.n_kv_heads, p.head_dim = n_q_heads, n_kv_heads, head_dim
+    p.window[:] = list(window)
+    p.block[:] = list(block)
+    p.rope_pairs[:] = list(rope_pairs)
+    p.rope_base, p.scale = rope_base, scale
+    p.dtype = PACK3D_BF16 if dtype == torch.bfloat16 else PACK3D_F32
+    p.gate_per_head = int(gate_per_head)
+    return p
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype] = None,
+         shape: Optional[tuple] = None, name: str = "") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise Pack3DError(rc, LIB.pack3d_last_error().decode())
+
+
+def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def pack3d_version() -> int:
+    return LIB.pack3d_version()
+
+
+def pack3d_backend_info() -> str:
+    return LIB.pack3d_backend_info().decode()
+
+
+def pack3d_last_error() -> str:
+    return LIB.pack3d_last_error().decode()
+
+
+def pack3d_forward_workspace_size(prob: Problem) -> int:
+    return LIB.pack3d_forward_workspace_size(ctypes.byref(prob))
+
+
+def pack3d_rope(prob: Problem, x: torch.Tensor, coords: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """R(c_i) x[i, h] for every token and head (out may be x: in place)."""
+    n, dt = prob.n_tokens, prob.torch_dtype
+    if x.dim() != 3:
+        raise ValueError("x must be [N, H, 64]")
+    heads = x.shape[1]
+    out = _empty(x.shape, dt, x) if out is None else out
+    _check(LIB.pack3d_rope(ctypes.byref(prob), _ptr(x, dt, (n, heads, 64), "x"),
+                           _ptr(out, dt, (n, heads, 64), "out"), heads,
+                           _ptr(coords, torch.int32, (n, 3), "coords"), _stream(x.device)))
+    return out
+
+
+def pack3d_block_summary(prob: Problem, k_cmp: torch.Tensor, v_cmp: torch.Tensor,
+                         a: Optional[torch.Tensor], cell_to_pos: torch.Tensor):
+    """Block summaries (k_sum, v_sum), each [Hkv, M, 64]."""
+    n, hkv, m, dt = prob.n_tokens, prob.n_kv_heads, prob.n_blocks, prob.torch_dtype
+    ks = _empty((hkv, m, 64), dt, k_cmp)
+    vs = _empty((hkv, m, 64), dt, k_cmp)
+    _check(LIB.pack3d_block_summary(
+        ctypes.byref(prob), _ptr(k_cmp, dt, (n, hkv, 64), "k_cmp"),
+        _ptr(v_cmp, dt, (n, hkv, 64), "v_cmp"), _ptr(a, torch.float32, (n, hkv), "a"),
+        _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"), ks.data_ptr(), vs.data_ptr(),
+        _stream(k_cmp.device)))
+    return ks, vs
+
+
+def pack3d_local_attn(prob: Problem, q_rot: torch.Tensor, k_rot: torch.Tensor, v: torch.Tensor,
+                      cell_to_pos: torch.Tensor, with_lse: bool = False):
+    """Local branch o_loc [N, Hq, 64] fp32 (and lse [N, Hq] if asked)."""
+    n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
+    o = _empty((n, hq, 64), torch.float32, q_rot)
+    lse = _empty((n, hq), torch.float32, q_rot) if with_lse else None
+    _check(LIB.pack3d_local_attn(
+        ctypes.byref(prob), _ptr(q_rot, dt, (n, hq, 64), "q_rot"),
+        _ptr(k_rot, dt, (n, hkv, 64), "k_rot"), _ptr(v, dt, (n, hkv, 64), "v"),
+        _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"), o.data_ptr(),
+        None if lse is None else lse.data_ptr(), _stream(q_rot.device)))
+    return (o, lse) if with_lse else o
+
+
+def pack3d_global_attn(prob: Problem, q_rot: torch.Tensor, k_sum: torch.Tensor,
+                       v_sum: torch.Tensor, with_lse: bool = False):
+    """Compressed branch o_cmp [N, Hq, 64] fp32 over all m = k_sum.shape[1] summaries."""
+    n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
+    m = k_sum.shape[1]
+    o = _empty((n, hq, 64), torch.float32, q_rot)
+    lse = _empty((n, hq), torch.float32, q_rot) if with_lse else None
+    _check(LIB.pack3d_global_attn(
+        ctypes.byref(prob), _ptr(q_rot, dt, (n, hq, 64), "q_rot"),
+        _ptr(k_sum, dt, (hkv, m, 64), "k_sum"), _ptr(v_sum, dt, (hkv, m, 64), "v_sum"), m,
+        o.data_ptr(), None if lse is None else lse.data_ptr(), _stream(q_rot.device)))
+    return (o, lse) if with_lse else o
+
+
+def pack3d_gate_mix(prob: Problem, o_loc: torch.Tensor, o_cmp: torch.Tensor,
+                    gate: torch.Tensor) -> torch.Tensor:
+    n, hq, dt = prob.n_tokens, prob.n_q_heads, prob.torch_dtype
+    gshape = (n, hq, 2) if prob.gate_per_head else (n, 2)
+    out = _empty((n, hq, 64), dt, o_loc)
+    _check(LIB.pack3d_gate_mix(
+        ctypes.byref(prob), _ptr(o_loc, torch.float32, (n, hq, 64), "o_loc"),
+        _ptr(o_cmp, torch.float32, (n, hq, 64), "o_cmp"),
+        _ptr(gate, torch.float32, gshape, "gate"), out.data_ptr(), _stream(o_loc.device)))
+    return out
+
+
+def alloc_workspace(prob: Problem, device) -> torch.Tensor:
+    """A caller-owned workspace of the size pack3d_forward needs (uint8)."""
+    size = pack3d_forward_workspace_size(prob)
+    if size == 0:
+        _check(LIB.pack3d_forward_workspace_size(ctypes.byref(prob)) or -2)
+    return torch.empty(size, dtype=torch.uint8, device=device)
+
+
+def pack3d_forward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
+                   workspace: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole forward: out [N, Hq, 64] in the input dtype."""
+    n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
+    gshape = (n, hq, 2) if prob.gate_per_head else (n, 2)
+    ws = alloc_workspace(prob, q.device) if workspace is None else workspace
+    out = _empty((n, hq, 64), dt, q) if out is None else out
+    _check(LIB.pack3d_forward(
+        ctypes.byref(prob), _ptr(q, dt, (n, hq, 64), "q"), _ptr(k_loc, dt, (n, hkv, 64), "k_loc"),
+        _ptr(v_loc, dt, (n, hkv, 64), "v_loc"), _ptr(k_cmp, dt, (n, hkv, 64), "k_cmp"),
+        _ptr(v_cmp, dt, (n, hkv, 64), "v_cmp"), _ptr(a, torch.float32, (n, hkv), "a"),
+        _ptr(coords, torch.int32, (n, 3), "coords"),
+        _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
+        _ptr(gate, torch.float32, gshape, "gate"), _ptr(out, dt, (n, hq, 64), "out"),
+        ws.data_ptr(), ws.numel(), _stream(q.device)))
+    return out
+
+
+def pack3d_build_cell_index(prob: Problem, coords: torch.Tensor) -> torch.Tensor:
+    n = prob.n_tokens
+    c2p = torch.empty(n, dtype=torch.int32, device=coords.device)
+    _check(LIB.pack3d_build_cell_index(ctypes.byref(prob),
+                                        _ptr(coords, torch.int32, (n, 3), "coords"),
+                                        c2p.data_ptr(), _stream(coords.device)))
+    return c2p
+
+
+def pack3d_check_packing(prob: Problem, coords: torch.Tensor, cell_to_pos: torch.Tensor) -> int:
+    """Number of tokens whose coordinates disagree with cell_to_pos (syncs)."""
+    n = prob.n_tokens
+    bad = torch.empty(1, dtype=torch.int32, device=coords.device)
+    _check(LIB.pack3d_check_packing(ctypes.byref(prob),
+                                     _ptr(coords, torch.int32, (n, 3), "coords"),
+                                     _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
+                                     bad.data_ptr(), _stream(coords.device)))
+    return int(bad.item())

@@ -1,0 +1,200 @@
+/*
+ * pack3d.h -- C ABI of libpack3d, the PACK3D local-global attention forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the one described in "Geometry Matters in Packed 3D
+ * Attention" (arXiv 2610.38694).  Citations below name the page and the
+ * passage: "notes" = the papernotes.org notes (method section, key designs
+ * 1-3, flowchart); "summary" = the ai.info summary (Methodology in Plain
+ * English).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tokens are stored in PACKED order: position i of every token-major array
+ *   is one lattice cell, coords[i] = (z, y, x) of that cell, and
+ *   cell_to_pos[(z*Y + y)*X + x] = i is the inverse map.  A packing is any
+ *   bijection between positions and cells (summary, Methodology: raster,
+ *   Morton, block-contiguous, random ...).  Results never depend on the
+ *   packing (notes, key design 1, Proposition 1): this library computes every
+ *   reduction in an order fixed by coordinates, so repacked outputs are the
+ *   permuted outputs bit for bit.
+ * - Arrays are dense, row-major, contiguous, device memory (HBM), owned by
+ *   the caller.  The library never allocates device memory and keeps no
+ *   state between calls except a per-thread error string.
+ * - "dtype" arrays hold float (PACK3D_F32) or bf16 (PACK3D_BF16) values as
+ *   chosen by pack3d_problem.dtype.  Accumulation is always fp32.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *   stream) and never synchronises the host.
+ * - Return value: PACK3D_OK or a negative pack3d_status.  Argument errors are
+ *   detected on the host, before any launch and without reading device data;
+ *   then nothing is launched and pack3d_last_error() describes the problem.
+ *   Unsupported shapes are errors (PACK3D_ERR_UNSUPPORTED); there is no
+ *   fallback path.  Data contracts (coordinates consistent with cell_to_pos,
+ *   weights normalised per block) are NOT checked on the hot path; use
+ *   pack3d_check_packing().  Out-of-range coordinates in coords or
+ *   cell_to_pos entries outside [0, N) are undefined behaviour.
+ */
+#ifndef PACK3D_H
+#define PACK3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PACK3D_VERSION 1
+
+typedef enum pack3d_status {
+  PACK3D_OK = 0,
+  PACK3D_ERR_NULL = -1,        /* a required pointer is NULL                   */
+  PACK3D_ERR_SHAPE = -2,       /* inconsistent sizes (grid, heads, block, ...) */
+  PACK3D_ERR_UNSUPPORTED = -3, /* valid but not implemented (e.g. head_dim)    */
+  PACK3D_ERR_WORKSPACE = -4,   /* workspace missing or too small               */
+  PACK3D_ERR_PACKING = -5,     /* reserved for packing-contract failures       */
+  PACK3D_ERR_HIP = -6          /* a HIP launch or runtime call failed          */
+} pack3d_status;
+
+typedef enum pack3d_dtype { PACK3D_F32 = 0, PACK3D_BF16 = 1 } pack3d_dtype;
+
+/*
+ * One operator instance.
+ *   grid[3]        lattice extents Z, Y, X (all >= 1); N = Z*Y*X < 2^31.
+ *   n_q_heads      Hq; n_kv_heads Hkv; Hq % Hkv == 0 and Hq/Hkv in
+ *                  {1,2,4,8,16,32} (query heads h read KV group h/(Hq/Hkv)).
+ *   head_dim       d_h; only 64 is supported.
+ *   window[3]      odd extents of the local box (notes, key design 3: the
+ *                  neighbourhood is a coordinate box); supported up to 3x7x7.
+ *                  The box is clipped at the lattice faces and holds the
+ *                  query cell itself.
+ *   block[3]       summary block shape (notes, key design 2); must divide
+ *                  grid; M = N / (block volume); volume <= 64.
+ *   rope_pairs[3]  rotary pairs on z, y, x (notes, key design 1: 11/11/10 at
+ *                  d_h = 64); 2*(sum) <= head_dim.  Pair p acts on dims
+ *                  (2p, 2p+1), z pairs first, with angle
+ *                  rope_base^(-r/m_a) * c_a for the r-th pair of axis a.
+ *   rope_base      10000 in the pages.
+ *   scale          softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   dtype          pack3d_dtype of q/k/v/out.
+ *   gate_per_head  0: gate logits are [N, 2]; 1: [N, Hq, 2].
+ */
+typedef struct pack3d_problem {
+  int32_t grid[3];
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t window[3];
+  int32_t block[3];
+  int32_t rope_pairs[3];
+  double rope_base;
+  float scale;
+  int32_t dtype;
+  int32_t gate_per_head;
+} pack3d_problem;
+
+/*
+ * Axial grid RoPE (notes, key design 1, the equation for R(c)):
+ *   y[i, h, :] = R(coords[i]) x[i, h, :]   for i < N, h < n_heads.
+ * x, y: dtype [N, n_heads, head_dim]; y may alias x (in place).
+ * coords: int32 [N, 3] (z, y, x) in [0, grid).
+ */
+int pack3d_rope(const pack3d_problem* prob, const void* x, void* y, int32_t n_heads,
+                const int32_t* coords, void* stream);
+
+/*
+ * Rotate-before-compression block summaries (notes, key design 2, the
+ * equations for k~_j and v~_j):
+ *   k_sum[g, j, :] = sum_{u in B_j} a[u, g] R(c_u) k_cmp[u, g, :]
+ *   v_sum[g, j, :] = sum_{u in B_j} a[u, g] v_cmp[u, g, :]
+ * B_j is the j-th aligned block in block-raster order,
+ *   j = ((z/bz)*(Y/by) + y/by)*(X/bx) + x/bx.
+ * k_cmp is NOT rotated (the rotation happens inside, before the sum).
+ * k_cmp, v_cmp: dtype [N, Hkv, head_dim].  a: fp32 [N, Hkv] or NULL for the
+ * uniform 1/v (normalisation is the caller's contract).  cell_to_pos: int32
+ * [N].  k_sum, v_sum: dtype [Hkv, M, head_dim], rounded once from fp32.
+ */
+int pack3d_block_summary(const pack3d_problem* prob, const void* k_cmp, const void* v_cmp,
+                         const float* a, const int32_t* cell_to_pos, void* k_sum,
+                         void* v_sum, void* stream);
+
+/*
+ * Exact local-neighbourhood attention (notes, key design 3; summary,
+ * Methodology, first contract):
+ *   o_loc[i, h] = sum_{u in N(i)} softmax_u(scale <q_rot[i,h], k_rot[u,g]>) v[u,g]
+ * with N(i) the clipped box window around coords[i].  q_rot: dtype
+ * [N, Hq, head_dim]; k_rot, v: dtype [N, Hkv, head_dim] (pre-rotated by
+ * pack3d_rope; v is never rotated).  o_loc: fp32 [N, Hq, head_dim];
+ * lse_loc: fp32 [N, Hq] natural-log log-sum-exp of the scaled logits, or NULL.
+ */
+int pack3d_local_attn(const pack3d_problem* prob, const void* q_rot, const void* k_rot,
+                      const void* v, const int32_t* cell_to_pos, float* o_loc,
+                      float* lse_loc, void* stream);
+
+/*
+ * Query -> all-summaries attention, streamed with an online softmax (notes,
+ * key design 3; summary, Methodology, second contract):
+ *   o_cmp[i, h] = sum_{j < m} softmax_j(scale <q_rot[i,h], k_sum[g,j]>) v_sum[g,j]
+ * q_rot: dtype [N, Hq, head_dim]; k_sum, v_sum: dtype [Hkv, m, head_dim]
+ * (m >= 1 is explicit, so m = N with 1x1x1 blocks is dense attention).
+ * o_cmp: fp32 [N, Hq, head_dim]; lse_cmp: fp32 [N, Hq] or NULL.
+ */
+int pack3d_global_attn(const pack3d_problem* prob, const void* q_rot, const void* k_sum,
+                       const void* v_sum, int32_t m, float* o_cmp, float* lse_cmp,
+                       void* stream);
+
+/*
+ * Tokenwise softmax gate (notes, flowchart node F and overall framework):
+ *   (g_loc, g_cmp) = softmax(gate_logits[i] or gate_logits[i, h])
+ *   out[i, h] = g_loc * o_loc[i, h] + g_cmp * o_cmp[i, h]
+ * Index 0 of the logits is the local branch.  o_loc, o_cmp: fp32
+ * [N, Hq, head_dim]; gate_logits: fp32 [N, 2] or [N, Hq, 2]; out: dtype.
+ */
+int pack3d_gate_mix(const pack3d_problem* prob, const float* o_loc, const float* o_cmp,
+                    const float* gate_logits, void* out, void* stream);
+
+/*
+ * The whole forward in the flowchart's order (notes, overall framework):
+ * RoPE on Q and K_loc, block summaries of (K_cmp, V_cmp), local attention,
+ * query->summary attention with the gate fused into its epilogue.
+ * q: dtype [N, Hq, 64]; k_loc, v_loc, k_cmp, v_cmp: dtype [N, Hkv, 64], all
+ * unrotated.  a: fp32 [N, Hkv] or NULL; coords: int32 [N, 3]; cell_to_pos:
+ * int32 [N]; gate_logits: fp32 [N, 2] or [N, Hq, 2]; out: dtype [N, Hq, 64].
+ * workspace: device memory of at least pack3d_forward_workspace_size() bytes,
+ * 256-byte aligned, caller-owned; it holds the rotated Q/K, the summaries and
+ * the fp32 local branch between the launches.
+ */
+int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
+                   const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                   const int32_t* coords, const int32_t* cell_to_pos,
+                   const float* gate_logits, void* out, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/* Bytes of workspace pack3d_forward needs for this problem (0 if invalid). */
+size_t pack3d_forward_workspace_size(const pack3d_problem* prob);
+
+/* cell_to_pos[(z*Y + y)*X + x] = i for every i < N (coords must be a
+ * bijection onto the lattice; entries of cells no token maps to are left
+ * unwritten). */
+int pack3d_build_cell_index(const pack3d_problem* prob, const int32_t* coords,
+                            int32_t* cell_to_pos, void* stream);
+
+/* Counts, into *n_bad_dev (device int32, overwritten), the tokens whose
+ * coordinates are outside the lattice or disagree with cell_to_pos. */
+int pack3d_check_packing(const pack3d_problem* prob, const int32_t* coords,
+                         const int32_t* cell_to_pos, int32_t* n_bad_dev, void* stream);
+
+/* Text of the last error on this thread ("" if none). */
+const char* pack3d_last_error(void);
+
+/* Which kernel variant serves each op (there are no fallbacks). */
+const char* pack3d_backend_info(void);
+
+/* PACK3D_VERSION of the built library. */
+int pack3d_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACK3D_H */

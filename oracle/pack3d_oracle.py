@@ -173,17 +173,20 @@ def local_window_sizes(coords: np.ndarray, grid: Sequence[int], window: Sequence
 
 def local_attention(q_rot: np.ndarray, k_rot: np.ndarray, v: np.ndarray,
                     coords: np.ndarray, grid: Sequence[int], window: Sequence[int],
-                    scale: float, rows: Optional[np.ndarray] = None, chunk: int = 8192):
+                    scale: float, rows: Optional[np.ndarray] = None, chunk: int = 8192,
+                    q_is_rows: bool = False):
     """o_loc[i,h] = sum_{u in N(i)} softmax_u(scale * <q_i,h, k_u,g>) v_u,g.
 
     Inputs are already rotated.  ``rows`` selects the query tokens computed
-    (default: all).  Returns ``(o_loc [R, Hq, D], lse [R, Hq])`` where ``lse``
-    is the natural-log log-sum-exp of the scaled logits.
+    (default: all); with ``q_is_rows`` the queries are given for those rows
+    only.  Returns ``(o_loc [R, Hq, D], lse [R, Hq])`` where ``lse`` is the
+    natural-log log-sum-exp of the scaled logits.
     """
     grid = tuple(int(g) for g in grid)
     if any(w % 2 == 0 for w in window):
         raise ValueError("window extents must be odd")
-    n, hq, d = q_rot.shape
+    n = k_rot.shape[0]
+    hq, d = q_rot.shape[1:]
     hkv = k_rot.shape[1]
     grp = hq // hkv
     coords = np.asarray(coords, np.int64)
@@ -197,7 +200,8 @@ def local_attention(q_rot: np.ndarray, k_rot: np.ndarray, v: np.ndarray,
     for s in range(0, len(rows), chunk):
         r = rows[s:s + chunk]
         nr = len(r)
-        qc = np.asarray(q_rot[r], np.float64).reshape(nr, hkv, grp, d)
+        qsel = np.arange(s, s + nr) if q_is_rows else r
+        qc = np.asarray(q_rot[qsel], np.float64).reshape(nr, hkv, grp, d)
         ci = coords[r]
         logit = np.full((nr, len(offs), hkv, grp), -np.inf)
         pos = np.zeros((nr, len(offs)), dtype=np.int64)
@@ -230,15 +234,18 @@ def local_attention(q_rot: np.ndarray, k_rot: np.ndarray, v: np.ndarray,
 # ----------------------------------------------------------------------------
 
 def global_attention(q_rot: np.ndarray, k_sum: np.ndarray, v_sum: np.ndarray,
-                     scale: float, rows: Optional[np.ndarray] = None):
+                     scale: float, rows: Optional[np.ndarray] = None, q_is_rows: bool = False):
     """o_cmp[i,h] = sum_{j<M} softmax_j(scale * <q_i,h, k~_j,g>) v~_j,g.
 
-    ``q_rot`` is ``[N, Hq, D]``; ``k_sum``/``v_sum`` are ``[Hkv, M, D]``.
-    Returns ``(o_cmp [R, Hq, D], lse [R, Hq])`` (natural-log log-sum-exp).
+    ``q_rot`` is ``[N, Hq, D]`` (or ``[R, Hq, D]`` with ``q_is_rows``);
+    ``k_sum``/``v_sum`` are ``[Hkv, M, D]``.  Returns
+    ``(o_cmp [R, Hq, D], lse [R, Hq])`` (natural-log log-sum-exp).
     """
     n, hq, d = q_rot.shape
     hkv, m, _ = k_sum.shape
     grp = hq // hkv
+    if q_is_rows:
+        q_rot, rows = q_rot, np.arange(n)
     rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
     out = np.zeros((len(rows), hq, d))
     lse = np.zeros((len(rows), hq))
@@ -289,15 +296,21 @@ def forward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits,
     ``p`` carries ``grid``, ``window``, ``block``, ``rope_pairs``,
     ``rope_base`` and ``head_dim``.  Arrays are in packed order.  With
     ``rows`` only those query tokens are computed (summaries are always
-    built in full).
+    built in full) and ``q_rot`` covers those rows only.
     """
     tau = 1.0 / math.sqrt(p.head_dim) if scale is None else scale
-    q_rot = rotate(q, coords, p.rope_pairs, p.rope_base)
+    coords = np.asarray(coords)
+    if rows is None:
+        q_rot = rotate(q, coords, p.rope_pairs, p.rope_base)
+    else:
+        rows = np.asarray(rows, np.int64)
+        q_rot = rotate(np.asarray(q)[rows], coords[rows], p.rope_pairs, p.rope_base)
     k_rot = rotate(k_loc, coords, p.rope_pairs, p.rope_base)
     k_sum, v_sum = block_summaries(k_cmp, v_cmp, a, coords, p.grid, p.block,
                                    p.rope_pairs, p.rope_base)
-    o_loc, lse_loc = local_attention(q_rot, k_rot, v_loc, coords, p.grid, p.window, tau, rows)
-    o_cmp, lse_cmp = global_attention(q_rot, k_sum, v_sum, tau, rows)
+    o_loc, lse_loc = local_attention(q_rot, k_rot, v_loc, coords, p.grid, p.window, tau, rows,
+                                     q_is_rows=rows is not None)
+    o_cmp, lse_cmp = global_attention(q_rot, k_sum, v_sum, tau, q_is_rows=rows is not None)
     g = gate_logits if rows is None else np.asarray(gate_logits)[rows]
     out = gate_mix(o_loc, o_cmp, g)
     return dict(out=out, o_loc=o_loc, o_cmp=o_cmp, lse_loc=lse_loc, lse_cmp=lse_cmp,

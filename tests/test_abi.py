@@ -1,0 +1,119 @@
+"""The C ABI on the CPU: the library loads, exports what include/pack3d.h
+declares, and rejects bad arguments on the host before any HIP call (no
+device is touched by these tests)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pack3d.h")
+
+
+@pytest.fixture(scope="module")
+def pk():
+    from geometry_aware_local_amd import pack3d
+    return pack3d
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(pack3d_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_header_declares_the_entry_points(pk):
+    names = _declared()
+    for required in ("pack3d_rope", "pack3d_block_summary", "pack3d_local_attn",
+                     "pack3d_global_attn", "pack3d_gate_mix", "pack3d_forward"):
+        assert required in names
+    assert set(names) == set(pk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(pk):
+    lib = ctypes.CDLL(pk.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_backend_info(pk):
+    assert pk.pack3d_version() == 1
+    info = pk.pack3d_backend_info()
+    assert "gfx950" in info and "no fallbacks" in info
+
+
+def _prob(pk, **kw):
+    base = dict(grid=(4, 16, 16), n_q_heads=2, n_kv_heads=1, window=(3, 5, 5), block=(1, 4, 4))
+    base.update(kw)
+    return pk.make_problem(**base)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(grid=(0, 16, 16)), -2, "grid"),
+    (dict(head_dim=32), -3, "head_dim"),
+    (dict(n_q_heads=3, n_kv_heads=2), -2, "multiple"),
+    (dict(window=(3, 4, 5)), -2, "odd"),
+    (dict(window=(3, 9, 5)), -3, "window"),
+    (dict(block=(1, 3, 4)), -2, "divide"),
+    (dict(block=(2, 8, 8)), -3, "volume"),
+    (dict(rope_pairs=(11, 11, 11)), -2, "rope_pairs"),
+    (dict(rope_base=-1.0), -2, "rope_base"),
+    (dict(grid=(2048, 1024, 1024)), -2, "int32"),
+])
+def test_bad_problems_are_rejected_on_the_host(pk, kw, code, text):
+    p = _prob(pk, **kw)
+    rc = pk.LIB.pack3d_rope(ctypes.byref(p), FAKE, FAKE, 2, FAKE, None)
+    assert rc == code
+    assert text in pk.pack3d_last_error()
+    assert pk.pack3d_forward_workspace_size(p) == 0
+
+
+def test_null_arguments_are_rejected(pk):
+    p = _prob(pk)
+    L, b = pk.LIB, ctypes.byref(p)
+    assert L.pack3d_rope(None, FAKE, FAKE, 2, FAKE, None) == -1
+    assert L.pack3d_rope(b, None, FAKE, 2, FAKE, None) == -1
+    assert L.pack3d_block_summary(b, FAKE, FAKE, None, None, FAKE, FAKE, None) == -1
+    assert L.pack3d_local_attn(b, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert L.pack3d_global_attn(b, FAKE, None, FAKE, 64, FAKE, None, None) == -1
+    assert L.pack3d_gate_mix(b, FAKE, FAKE, None, FAKE, None) == -1
+    assert L.pack3d_build_cell_index(b, None, FAKE, None) == -1
+    assert L.pack3d_check_packing(b, FAKE, FAKE, None, None) == -1
+    args = [FAKE] * 5 + [None] + [FAKE] * 4
+    assert L.pack3d_forward(b, *args, None, 10 ** 9, None) == -4      # no workspace
+    assert "workspace" in pk.pack3d_last_error()
+    assert L.pack3d_forward(b, *args, FAKE, 16, None) == -4           # too small
+    assert L.pack3d_forward(b, *args, FAKE + 8, 10 ** 9, None) == -4  # misaligned
+    assert "aligned" in pk.pack3d_last_error()
+    assert L.pack3d_global_attn(b, FAKE, FAKE, FAKE, 0, FAKE, None, None) == -2
+    assert L.pack3d_rope(b, FAKE, FAKE, 0, FAKE, None) == -2
+
+
+def test_unsupported_group_ratio(pk):
+    p = _prob(pk, n_q_heads=32, n_kv_heads=1)
+    b = ctypes.byref(p)
+    assert pk.LIB.pack3d_local_attn(b, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -3
+    assert "Hq/Hkv" in pk.pack3d_last_error()
+
+
+def test_workspace_size_matches_layout(pk):
+    p = _prob(pk, grid=(64, 64, 64), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
+    n, m = 64 ** 3, 64 ** 3 // 16
+    bf16 = 2 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) + 4 * n * 8 * 64
+    assert pk.pack3d_forward_workspace_size(p) == bf16
+    p.dtype = 0
+    assert pk.pack3d_forward_workspace_size(p) == 4 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) \
+        + 4 * n * 8 * 64
+
+
+def test_error_string_is_per_call(pk):
+    p = _prob(pk, head_dim=16)
+    assert pk.LIB.pack3d_rope(ctypes.byref(p), FAKE, FAKE, 1, FAKE, None) == -3
+    assert pk.pack3d_last_error() != ""
+    assert pk.pack3d_forward_workspace_size(_prob(pk)) > 0
+    assert pk.pack3d_last_error() == ""

@@ -1,0 +1,388 @@
+"""GPU parity: every libpack3d entry point against the fp64 oracle.
+
+The HIP path is called through the C ABI (ctypes binding); expected values come
+from ``oracle/`` only.  Small workloads are compared element by element in
+full; the 262 144- and 1 048 576-token workloads on sampled query rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthgen as sg
+from oracle import pack3d_oracle as orc
+from tests import gpu_util as gu
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
+
+W = sg.WORKLOADS
+TINY = W["tiny_f32_4x16x16"]
+MORTON = W["morton_bf16_16x64x64"]
+BLOCK = W["block_bf16_64x64x64"]
+RANDOM = W["random_bf16_64x128x128"]
+
+
+def _w(name, grid, hq, hkv, dtype, window=(3, 7, 7), block=(1, 4, 4), packing="random",
+       weights="softmax", seed=7):
+    return sg.Workload(name, grid, packing, hq, hkv, window, block, dtype, weights, seed)
+
+
+# Small cases that span several tiles and ragged tails: Y, X not multiples of
+# the 8x8 local tile, M not a multiple of the 64-key summary tile, every
+# supported heads-per-group ratio, both dtypes.
+SMALL = [
+    TINY,
+    _w("ragged_f32_g4", (3, 12, 20), 4, 1, "f32"),
+    _w("ragged_bf16_g4", (3, 12, 20), 8, 2, "bf16"),
+    _w("g1_bf16", (2, 8, 12), 2, 2, "bf16", packing="morton"),
+    _w("g8_f32", (4, 8, 8), 8, 1, "f32", window=(3, 3, 5)),
+    _w("g16_bf16", (2, 16, 8), 16, 1, "bf16", window=(1, 7, 3)),
+    _w("g2_bf16_uniform", (5, 8, 16), 4, 2, "bf16", window=(5, 5, 5), weights="uniform",
+       packing="block"),
+    _w("tiny_lattice_f32", (1, 4, 4), 4, 2, "f32", window=(3, 7, 7)),
+]
+IDS = [w.name for w in SMALL]
+
+
+@pytest.fixture(scope="module")
+def pk():
+    from geometry_aware_local_amd import pack3d
+    return pack3d
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _rows(w, k, seed=0):
+    n = w.n_tokens
+    return np.arange(n) if n <= k else np.sort(np.random.default_rng(seed).choice(n, k, False))
+
+
+# --------------------------------------------------------------------------
+# single ops, fed with the oracle's own (rounded) inputs
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", SMALL + [MORTON], ids=IDS + [MORTON.name])
+def test_rope(pk, w):
+    _say("rope", w.name)
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    got_q = gu.host(pk.pack3d_rope(prob, d["q"], d["coords"]))
+    k = d["k_loc"].clone()
+    pk.pack3d_rope(prob, k, d["coords"], out=k)                 # in place
+    for got, x in ((got_q, inp.q), (gu.host(k), inp.k_loc)):
+        ref = orc.rotate(x, inp.coords, w.rope_pairs, w.rope_base)
+        err = np.abs(got - ref)
+        if w.dtype == "f32":
+            assert err.max() <= 1e-5
+        else:
+            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+@pytest.mark.parametrize("w", SMALL + [MORTON], ids=IDS + [MORTON.name])
+def test_block_summary(pk, w):
+    _say("block_summary", w.name)
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    ks, vs = pk.pack3d_block_summary(prob, d["k_cmp"], d["v_cmp"], d["a"], d["cell_to_pos"])
+    rk, rv = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block,
+                                 w.rope_pairs, w.rope_base)
+    for got, ref in ((gu.host(ks), rk), (gu.host(vs), rv)):
+        if w.dtype == "f32":
+            assert gu.max_abs(got, ref) <= 1e-5
+        else:
+            assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+def _rotated(w, inp):
+    q = gu.round_like(orc.rotate(inp.q, inp.coords, w.rope_pairs, w.rope_base), w)
+    k = gu.round_like(orc.rotate(inp.k_loc, inp.coords, w.rope_pairs, w.rope_base), w)
+    return q, k
+
+
+@pytest.mark.parametrize("w", SMALL + [MORTON], ids=IDS + [MORTON.name])
+def test_local_attn(pk, w):
+    _say("local_attn", w.name)
+    inp = sg.make_inputs(w)
+    dt = gu.tdtype(w)
+    q, k = _rotated(w, inp)
+    prob = gu.problem(pk, w)
+    o, lse = pk.pack3d_local_attn(prob, gu.dev(q, dt), gu.dev(k, dt), gu.dev(inp.v_loc, dt),
+                                  gu.dev(inp.cell_to_pos), with_lse=True)
+    rows = _rows(w, 4096)
+    ro, rl = orc.local_attention(q, k, inp.v_loc, inp.coords, w.grid, w.window, 0.125, rows)
+    go, gl = gu.host(o)[rows], gu.host(lse)[rows]
+    assert gu.max_rel(go, ro) <= gu.REL_TOL[w.dtype]
+    assert gu.max_abs(gl, rl) <= (1e-5 if w.dtype == "f32" else 1e-3)
+
+
+@pytest.mark.parametrize("w", SMALL + [MORTON], ids=IDS + [MORTON.name])
+def test_global_attn(pk, w):
+    _say("global_attn", w.name)
+    inp = sg.make_inputs(w)
+    dt = gu.tdtype(w)
+    q, _ = _rotated(w, inp)
+    rk, rv = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block,
+                                 w.rope_pairs, w.rope_base)
+    rk, rv = gu.round_like(rk, w), gu.round_like(rv, w)
+    prob = gu.problem(pk, w)
+    o, lse = pk.pack3d_global_attn(prob, gu.dev(q, dt), gu.dev(rk, dt), gu.dev(rv, dt),
+                                   with_lse=True)
+    rows = _rows(w, 2048)
+    ro, rl = orc.global_attention(q, rk, rv, 0.125, rows)
+    assert gu.max_rel(gu.host(o)[rows], ro) <= gu.REL_TOL[w.dtype]
+    assert gu.max_abs(gu.host(lse)[rows], rl) <= (1e-5 if w.dtype == "f32" else 1e-3)
+
+
+@pytest.mark.parametrize("w", [TINY, MORTON.with_(grid=(4, 16, 16))], ids=["f32", "bf16"])
+@pytest.mark.parametrize("per_head", [False, True])
+def test_gate_mix(pk, w, per_head):
+    _say("gate_mix", w.name, per_head)
+    rng = np.random.default_rng(5)
+    n, hq = w.n_tokens, w.n_q_heads
+    ol = rng.standard_normal((n, hq, 64)).astype(np.float32)
+    oc = rng.standard_normal((n, hq, 64)).astype(np.float32)
+    g = rng.standard_normal((n, hq, 2) if per_head else (n, 2)).astype(np.float32) * 3
+    prob = gu.problem(pk, w, gate_per_head=per_head)
+    out = gu.host(pk.pack3d_gate_mix(prob, gu.dev(ol), gu.dev(oc), gu.dev(g)))
+    ref = orc.gate_mix(ol, oc, g)
+    err = np.abs(out - ref)
+    if w.dtype == "f32":
+        assert err.max() <= 1e-6
+    else:
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+# --------------------------------------------------------------------------
+# the whole path
+# --------------------------------------------------------------------------
+
+def _check_forward(pk, w, inp, rows):
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    out = pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"],
+                            d["coords"], d["cell_to_pos"], d["gate"])
+    # the same chain through the split entry points, for per-branch checks
+    q_rot = pk.pack3d_rope(prob, d["q"], d["coords"])
+    k_rot = pk.pack3d_rope(prob, d["k_loc"], d["coords"])
+    ks, vs = pk.pack3d_block_summary(prob, d["k_cmp"], d["v_cmp"], d["a"], d["cell_to_pos"])
+    o_loc = pk.pack3d_local_attn(prob, q_rot, k_rot, d["v_loc"], d["cell_to_pos"])
+    o_cmp = pk.pack3d_global_attn(prob, q_rot, ks, vs)
+    torch.cuda.synchronize()
+    ref = orc.forward(w, inp.q, inp.k_loc, inp.v_loc, inp.k_cmp, inp.v_cmp, inp.a, inp.coords,
+                      inp.gate, rows=rows)
+    got = gu.host(out)[rows]
+    assert gu.max_abs(got, ref["out"]) <= gu.ABS_TOL[w.dtype]
+    assert gu.max_rel(gu.host(o_loc)[rows], ref["o_loc"]) <= gu.REL_TOL[w.dtype]
+    assert gu.max_rel(gu.host(o_cmp)[rows], ref["o_cmp"]) <= gu.REL_TOL[w.dtype]
+    # the split chain's gate gives the fused forward's result
+    mixed = pk.pack3d_gate_mix(prob, o_loc, o_cmp, d["gate"])
+    assert gu.max_abs(gu.host(mixed), gu.host(out)) <= (1e-6 if w.dtype == "f32" else 1e-2)
+    return out, o_loc, o_cmp, ref
+
+
+@pytest.mark.parametrize("w", SMALL, ids=IDS)
+def test_forward_small(pk, w):
+    _say("forward", w.name)
+    inp = sg.make_inputs(w)
+    _check_forward(pk, w, inp, np.arange(w.n_tokens))
+
+
+def test_forward_65k_morton(pk):
+    _say("forward", MORTON.name)
+    inp = sg.make_inputs(MORTON)
+    _check_forward(pk, MORTON, inp, _rows(MORTON, 4096))
+
+
+def test_branches_with_peaked_queries(pk):
+    """Queries scaled by 4 make both softmaxes far from uniform.  The kernels
+    get the rotated queries/keys and summaries as stored on the device (bf16
+    values), and so does the oracle, so only the kernels' own arithmetic is
+    measured; both branches are held to the relative bound."""
+    w = MORTON
+    _say("branches peaked", w.name)
+    inp = sg.make_inputs(w)
+    inp.q = (inp.q * 4.0).astype(np.float32)        # exact in bf16
+    dt = gu.tdtype(w)
+    q, k = _rotated(w, inp)
+    rk, rv = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block)
+    rk, rv = gu.round_like(rk, w), gu.round_like(rv, w)
+    prob = gu.problem(pk, w)
+    o_loc = pk.pack3d_local_attn(prob, gu.dev(q, dt), gu.dev(k, dt), gu.dev(inp.v_loc, dt),
+                                 gu.dev(inp.cell_to_pos))
+    o_cmp = pk.pack3d_global_attn(prob, gu.dev(q, dt), gu.dev(rk, dt), gu.dev(rv, dt))
+    rows = _rows(w, 2048, seed=1)
+    ro_loc, _ = orc.local_attention(q, k, inp.v_loc, inp.coords, w.grid, w.window, 0.125, rows)
+    ro_cmp, _ = orc.global_attention(q, rk, rv, 0.125, rows)
+    assert gu.max_rel(gu.host(o_loc)[rows], ro_loc) <= gu.REL_TOL["bf16"]
+    assert gu.max_rel(gu.host(o_cmp)[rows], ro_cmp) <= gu.REL_TOL["bf16"]
+
+
+def test_forward_262k_block_sampled(pk):
+    _say("forward", BLOCK.name)
+    inp = sg.make_inputs(BLOCK)
+    _check_forward(pk, BLOCK, inp, _rows(BLOCK, 1024, seed=2))
+
+
+def test_forward_1m_random_sampled(pk):
+    _say("forward", RANDOM.name)
+    inp = sg.make_inputs(RANDOM)
+    rows = _rows(RANDOM, 256, seed=3)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, RANDOM)
+    out = pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"],
+                            d["coords"], d["cell_to_pos"], d["gate"])
+    ref = orc.forward(RANDOM, inp.q, inp.k_loc, inp.v_loc, inp.k_cmp, inp.v_cmp, inp.a,
+                      inp.coords, inp.gate, rows=rows)
+    assert gu.max_abs(gu.host(out)[rows], ref["out"]) <= gu.ABS_TOL["bf16"]
+
+
+# --------------------------------------------------------------------------
+# packing equivariance (Proposition 1): repacked outputs are the permuted
+# outputs, bit for bit
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [BLOCK, TINY], ids=["262k_bf16", "tiny_f32"])
+def test_packing_equivariance(pk, w):
+    _say("equivariance", w.name)
+    base = sg.make_inputs(w.with_(packing="raster"))
+    prob = gu.problem(pk, w)
+    outs = {}
+    for kind in ("raster", "block", "random", "morton"):
+        inp = base if kind == "raster" else base.repacked(kind)
+        d = gu.device_inputs(inp)
+        out = pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"],
+                                d["a"], d["coords"], d["cell_to_pos"], d["gate"])
+        back = torch.from_numpy(inp.cell_to_pos[base.order].astype(np.int64)).cuda()
+        outs[kind] = out[back].float()
+    for kind in ("block", "random", "morton"):
+        diff = (outs[kind] - outs["raster"]).abs().max().item()
+        assert diff <= 1e-6, (kind, diff)
+        assert torch.equal(outs[kind], outs["raster"]), kind
+
+
+def test_repeat_runs_are_bitwise_equal(pk):
+    _say("determinism", MORTON.name)
+    inp = sg.make_inputs(MORTON)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, MORTON)
+    args = (d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"], d["coords"],
+            d["cell_to_pos"], d["gate"])
+    a = pk.pack3d_forward(prob, *args)
+    b = pk.pack3d_forward(prob, *args)
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# degenerate cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unit_blocks_give_dense_attention(pk, dtype):
+    """1x1x1 blocks with a = 1 turn the compressed branch into dense
+    axial-RoPE attention over (R(c)Q, R(c)K_cmp, V_cmp)."""
+    w = _w("dense", (4, 8, 10), 8, 2, dtype, block=(1, 1, 1), weights="uniform")
+    _say("dense", dtype)
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    q_rot = pk.pack3d_rope(prob, d["q"], d["coords"])
+    ks, vs = pk.pack3d_block_summary(prob, d["k_cmp"], d["v_cmp"], None, d["cell_to_pos"])
+    assert ks.shape[1] == w.n_tokens
+    o = gu.host(pk.pack3d_global_attn(prob, q_rot, ks, vs))
+    qr = orc.rotate(inp.q, inp.coords)
+    kr = orc.rotate(inp.k_cmp, inp.coords)
+    hq, grp = w.n_q_heads, w.n_q_heads // w.n_kv_heads
+    ref = np.zeros_like(o)
+    for h in range(hq):
+        s = 0.125 * qr[:, h] @ kr[:, h // grp].T
+        p = np.exp(s - s.max(1, keepdims=True))
+        ref[:, h] = (p / p.sum(1, keepdims=True)) @ inp.v_cmp[:, h // grp].astype(np.float64)
+    assert gu.max_abs(o, ref) <= gu.ABS_TOL[dtype]
+    assert gu.max_rel(o, ref) <= gu.REL_TOL[dtype]
+
+
+def test_window_of_one_cell_returns_values(pk):
+    """A 1x1x1 window attends only to the query cell: o_loc = V_loc."""
+    w = _w("w1", (3, 8, 12), 4, 2, "f32", window=(1, 1, 1), weights="uniform")
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    o = gu.host(pk.pack3d_local_attn(prob, d["q"], d["k_loc"], d["v_loc"], d["cell_to_pos"]))
+    want = np.repeat(inp.v_loc, 2, axis=1)
+    assert gu.max_abs(o, want) <= 1e-6
+
+
+# --------------------------------------------------------------------------
+# test power: planted mistakes (in the oracle, on the CPU) must fail the checks
+# --------------------------------------------------------------------------
+
+def test_checks_catch_planted_mistakes(pk):
+    w = MORTON.with_(grid=(4, 32, 32))
+    _say("planted mistakes", w.name)
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    q_rot = pk.pack3d_rope(prob, d["q"], d["coords"])
+    ks, vs = pk.pack3d_block_summary(prob, d["k_cmp"], d["v_cmp"], d["a"], d["cell_to_pos"])
+    o_cmp = gu.host(pk.pack3d_global_attn(prob, q_rot, ks, vs))
+    qr = orc.rotate(inp.q, inp.coords)
+    good_k, good_v = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block)
+    good, _ = orc.global_attention(qr, good_k, good_v, 0.125)
+    assert gu.max_rel(o_cmp, good) <= gu.REL_TOL["bf16"]
+    # 1. summaries shuffled (keys paired with another block's values)
+    perm = np.random.default_rng(0).permutation(good_v.shape[1])
+    bad, _ = orc.global_attention(qr, good_k, good_v[:, perm], 0.125)
+    assert gu.max_rel(o_cmp, bad) > gu.REL_TOL["bf16"]
+    # 2. keys pooled without rotation
+    nz = np.zeros_like(inp.coords)
+    bk, bv = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block,
+                                 rope_coords=nz)
+    bad, _ = orc.global_attention(qr, bk, bv, 0.125)
+    assert gu.max_rel(o_cmp, bad) > gu.REL_TOL["bf16"]
+    # 3. packed index used as the coordinate of the rotation
+    seq = np.stack([np.zeros(w.n_tokens), np.zeros(w.n_tokens), np.arange(w.n_tokens)], 1)
+    bad, _ = orc.global_attention(orc.rotate(inp.q, seq.astype(np.int64)), good_k, good_v, 0.125)
+    assert gu.max_rel(o_cmp, bad) > gu.REL_TOL["bf16"]
+    # 4. the compressed branch dropped altogether is caught by the relative
+    #    branch check ...
+    assert gu.max_rel(np.zeros_like(o_cmp), good) > gu.REL_TOL["bf16"]
+    # ... while at 262 144 tokens the absolute end-to-end bound alone could not
+    #     see it: the whole branch is smaller than that bound there
+    big = sg.make_inputs(BLOCK)
+    rows = _rows(BLOCK, 64, seed=4)
+    ref = orc.forward(BLOCK, big.q, big.k_loc, big.v_loc, big.k_cmp, big.v_cmp, big.a,
+                      big.coords, big.gate, rows=rows)
+    assert np.abs(ref["o_cmp"]).max() < gu.ABS_TOL["bf16"]
+
+
+# --------------------------------------------------------------------------
+# helpers and argument errors on the device path
+# --------------------------------------------------------------------------
+
+def test_cell_index_and_packing_check(pk):
+    w = MORTON.with_(grid=(4, 16, 16))
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    c2p = pk.pack3d_build_cell_index(prob, d["coords"])
+    assert torch.equal(c2p.cpu(), torch.from_numpy(inp.cell_to_pos))
+    assert pk.pack3d_check_packing(prob, d["coords"], d["cell_to_pos"]) == 0
+    bad = d["cell_to_pos"].clone()
+    bad[[3, 7]] = bad[[7, 3]]
+    assert pk.pack3d_check_packing(prob, d["coords"], bad) == 2
+
+
+def test_workspace_too_small_is_rejected(pk):
+    inp = sg.make_inputs(TINY)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, TINY)
+    ws = torch.empty(pk.pack3d_forward_workspace_size(prob) - 256, dtype=torch.uint8,
+                     device="cuda")
+    with pytest.raises(pk.Pack3DError, match="ERR_WORKSPACE"):
+        pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"],
+                          d["coords"], d["cell_to_pos"], d["gate"], workspace=ws)

@@ -391,3 +391,14 @@ def test_bf16_rounding_is_nearest_even():
     got = sg.round_to_bf16(x)
     want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(got, want)
+
+
+def test_sampled_rows_equal_full_rows():
+    """Computing a subset of query rows gives those rows of the full result."""
+    w = _small(packing="random")
+    inp = sg.make_inputs(w)
+    full = _fwd(inp)
+    rows = np.array([0, 5, 17, 100, w.n_tokens - 1])
+    part = _fwd(inp, rows=rows)
+    for key in ("out", "o_loc", "o_cmp", "lse_loc", "lse_cmp"):
+        assert np.abs(part[key] - full[key][rows]).max() <= 1e-13, key
