@@ -6,22 +6,38 @@
 // vectors are materialised.  The gate (flowchart node F) mixes the result
 // with the local branch per token.
 //
-// Design (gfx950): one workgroup = 8 waves = one KV group and 512 (bf16) query
-// rows, where a query row is a (token, head) pair of that group, so the G
-// heads sharing the group's summaries are stacked as MFMA columns and every
-// summary tile staged in LDS feeds all of them.  Summary tiles of 64 keys are
-// double-buffered in LDS (K row-major swizzled, V transposed); each wave
-// computes S^T = K Q^T and O^T += V^T P^T with 32x32 MFMA tiles (see
-// pack3d_device.h) and keeps its softmax state in registers.  Workgroups are
-// ordered so that all the workgroups an XCD receives read the same KV group,
-// keeping one group's summaries resident in that XCD's L2.
+// Design (gfx950):
+// * One workgroup = 8 waves = one KV group and 512 (bf16) query rows, a query
+//   row being a (token, head) pair of that group: the G heads sharing the
+//   group's summaries are stacked as MFMA columns, so every summary tile
+//   staged in LDS feeds all of them.
+// * Summary tiles of 64 keys are double-buffered in LDS as plain row-major
+//   copies (16-byte chunks XOR-swizzled against bank conflicts).  Each wave
+//   computes S^T = K Q^T and O^T += V^T P^T with 32x32 MFMA tiles (see
+//   pack3d_device.h); the V^T operand comes straight from the row-major tile
+//   through the gfx950 transposing LDS read (ds_read_b64_tr_b16).
+// * Softmax reference.  The kernel is bound by the VALU work per logit, so
+//   the running max is avoided where a bound allows: given the largest
+//   summary norm of the group (kmax), every logit of query q lies within
+//   +-|q| kmax (Cauchy-Schwarz).  A query whose bound B is small uses the
+//   fixed reference max(0, B - 64) for the whole stream (its exponentials
+//   stay in [2^-96, 2^64]); only queries with a large bound track a lazily
+//   updated running max.  The choice is per query, so results do not depend
+//   on which queries share a wave (packing equivariance stays bitwise).
+// * Workgroups are ordered so that all the workgroups an XCD receives read
+//   the same KV group, keeping one group's summaries resident in its L2.
 #include "pack3d_device.h"
 
 namespace pack3d {
 
 constexpr int kGWaves = 8;
 constexpr int kGKt = 64;           // keys per LDS tile
-constexpr int kGVld = kGKt + 4;    // V^T row pitch (elements)
+constexpr int kGVld = kGKt + 4;    // fp32 V^T row pitch (elements)
+constexpr float kRefHeadroom = 64.0f;   // fixed reference keeps exponentials <= 2^64
+constexpr float kSafeBound = 80.0f;     // ... for logit bounds up to this (log2 units)
+constexpr float kBoundMargin = 1.015625f;  // covers bf16 rounding of q, k~ and fp32 sums
+
+enum GMode : int { kGeneral = 0, kFixedRef = 1, kZeroRef = 2 };
 
 template <typename T> struct GCfg { static constexpr int kCb = 2; };   // column blocks / wave
 template <> struct GCfg<float> { static constexpr int kCb = 1; };
@@ -34,16 +50,31 @@ struct GArgs {
   int64_t m;
   int64_t n;
   int32_t hq, hkv, grp;
-  float c;                 // softmax scale * log2(e)
+  float c;                 // multiplier of q.k~ giving log2-domain logits
   float* o_cmp;
   float* lse;
   const float* o_loc;
   const float* gate;
   T* out;
+  const float* kmax;       // [Hkv] max_j c |k~_j| (NULL: always track the max)
   int32_t gate_per_head;
   int64_t tiles;           // query tiles per KV group
   int32_t xcd_per;         // consecutive XCDs sharing a group (0: plain order)
 };
+
+// ---------------------------------------------------------------------------
+// LDS tiles.  bf16: K and V both row-major [64 keys][64 dims], chunk c of key
+// row r stored at chunk c ^ (r & 7) (K) or c ^ (2r & 6) (V: the transposing
+// read takes 4 consecutive keys x 16 dims per 16 lanes).  fp32: K as above,
+// V transposed [64 dims][kGVld].
+// ---------------------------------------------------------------------------
+template <typename T>
+struct GLds {
+  static constexpr bool kF32 = std::is_same<T, float>::value;
+  static constexpr int kVElems = kF32 ? 64 * kGVld : kGKt * 64;
+};
+
+__device__ __forceinline__ int v_swz(int row, int chunk) { return chunk ^ ((2 * row) & 6); }
 
 template <typename T>
 struct GStage {
@@ -78,18 +109,24 @@ __device__ __forceinline__ void g_store(const GStage<T>& st, T* kl, T* vl, int t
     const int idx = tid + c * kGWaves * 64;
     const int row = idx / (64 / GStage<T>::kE), ch = idx % (64 / GStage<T>::kE);
     st16(kl + KLds<T>::chunk_off(row, ch), st.k[c]);
-    const T* e = reinterpret_cast<const T*>(&st.v[c]);
+    if constexpr (GLds<T>::kF32) {
+      const T* e = reinterpret_cast<const T*>(&st.v[c]);
 #pragma unroll
-    for (int i = 0; i < GStage<T>::kE; ++i) vl[(ch * GStage<T>::kE + i) * kGVld + row] = e[i];
+      for (int i = 0; i < GStage<T>::kE; ++i) vl[(ch * GStage<T>::kE + i) * kGVld + row] = e[i];
+    } else {
+      st16(vl + row * 64 + v_swz(row, ch) * 8, st.v[c]);
+    }
   }
 }
 
-// A operand of PV step t for head dim `dim`, key block starting at kb0.
+// A operand (V^T) of PV step t for head dim `dim` = db*32 + lane%32, key block
+// kb0 .. kb0+31.
 template <typename T>
-__device__ __forceinline__ void v_frags(typename Mma<T>::frag* f, const T* vl, int dim, int kb0,
-                                        int h) {
-  const T* r = vl + dim * kGVld + kb0;
-  if constexpr (std::is_same<T, float>::value) {
+__device__ __forceinline__ void v_frags(typename Mma<T>::frag* f, const T* vl, int db, int kb0,
+                                        int lane) {
+  const int h = lane >> 5;
+  if constexpr (GLds<T>::kF32) {
+    const T* r = vl + (db * 32 + (lane & 31)) * kGVld + kb0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 x = *reinterpret_cast<const f32x4*>(r + 8 * q + 4 * h);
@@ -97,15 +134,135 @@ __device__ __forceinline__ void v_frags(typename Mma<T>::frag* f, const T* vl, i
       for (int j = 0; j < 4; ++j) f[4 * q + j] = x[j];
     }
   } else {
+    // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+    // (i % 4) of the 8-byte chunks addressed by lanes i/4, i/4+4, i/4+8,
+    // i/4+12.  Lane r addresses key K0 + r/4, dims base + 4*(r%4) .. +3, so
+    // lane i receives dim base + i of keys K0 .. K0+3.
+    const int r = lane & 15;
+    const int dim = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (r & 3);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(r + 16 * t + 4 * h);
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(r + 16 * t + 8 + 4 * h);
+      bf16x4 part[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key = kb0 + 16 * t + 8 * half + 4 * h + (r >> 2);
+        const T* p = vl + key * 64 + v_swz(key, dim >> 3) * 8 + (dim & 7);
+        part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(
+                (__attribute__((address_space(3))) char*)p));
+      }
       bf16x8 x;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { x[j] = lo[j]; x[4 + j] = hi[j]; }
+      for (int j = 0; j < 4; ++j) {
+        x[j] = part[0][j];
+        x[4 + j] = part[1][j];
+      }
       f[t] = x;
     }
+  }
+}
+
+// Per-column softmax state.
+struct GCol {
+  float m;       // reference (log2 units)
+  float l;       // this lane's partial sum
+  bool track;    // true: lazily tracked running max; false: fixed reference
+};
+
+// One 64-key tile for all of the wave's column blocks.
+template <typename T, int CB, int MODE>
+__device__ __forceinline__ void g_tile(const T* kl, const T* vl, int64_t k0, int64_t m,
+                                       float c, const QFrag<T> (&qf)[CB], GCol (&st)[CB],
+                                       f32x16 (&o)[CB][2], int lane) {
+  const int h = lane >> 5, col = lane & 31;
+  f32x16 s[2][CB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    KFrag<T> kf;
+    load_kfrag<T>(kf, kl, kb * 32 + col, h);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) s[kb][cb] = qk_tile<T>(kf, qf[cb]);
+  }
+  if (k0 + kGKt > m) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t key = k0 + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (key >= m)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) s[kb][cb][v] = kNegInf;
+      }
+  }
+
+  typename Mma<T>::frag pf[2][CB][Mma<T>::kPvSteps];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    if constexpr (MODE == kGeneral) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][cb][v]);
+      const float mt = pair_max(mx) * c;
+      const bool upd = st[cb].track && mt > st[cb].m + kRescaleSlack;
+      if (__any(upd)) {
+        const float mn = upd ? mt : st[cb].m;
+        const float alpha = upd ? __builtin_amdgcn_exp2f(st[cb].m - mn) : 1.0f;
+        st[cb].m = mn;
+        st[cb].l *= alpha;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          o[cb][0][v] *= alpha;
+          o[cb][1][v] *= alpha;
+        }
+      }
+    }
+    const float mu = st[cb].m == kNegInf ? 0.0f : st[cb].m;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 p;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        if constexpr (MODE == kZeroRef)
+          p[v] = __builtin_amdgcn_exp2f(s[kb][cb][v]);
+        else
+          p[v] = __builtin_amdgcn_exp2f(fmaf(s[kb][cb][v], c, -mu));
+      }
+#pragma unroll
+      for (int t = 0; t < Mma<T>::kPvSteps; ++t) {
+        pf[kb][cb][t] = Mma<T>::p_frag(p, t);
+        st[cb].l = frag_sum(pf[kb][cb][t], st[cb].l);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      typename Mma<T>::frag vf[Mma<T>::kPvSteps];
+      v_frags<T>(vf, vl, db, kb * 32, lane);
+#pragma unroll
+      for (int t = 0; t < Mma<T>::kPvSteps; ++t)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][db] = Mma<T>::mma(vf[t], pf[kb][cb][t], o[cb][db]);
+    }
+}
+
+template <typename T, int CB, int MODE>
+__device__ __forceinline__ void g_stream(T (&k_lds)[2][kGKt * 64],
+                                         T (&v_lds)[2][GLds<T>::kVElems], GStage<T>& stage,
+                                         const T* ksg, const T* vsg, const GArgs<T>& A,
+                                         const QFrag<T> (&qf)[CB], GCol (&st)[CB],
+                                         f32x16 (&o)[CB][2], int tid, int lane) {
+  const int64_t nt = (A.m + kGKt - 1) / kGKt;
+  for (int64_t t = 0; t < nt; ++t) {
+    const int b = (int)(t & 1);
+    g_store<T>(stage, k_lds[b], v_lds[b], tid);
+    __syncthreads();
+    if (t + 1 < nt) g_load<T>(stage, ksg, vsg, (t + 1) * kGKt, A.m, tid);
+    g_tile<T, CB, MODE>(k_lds[b], v_lds[b], t * kGKt, A.m, A.c, qf, st, o, lane);
   }
 }
 
@@ -114,7 +271,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   constexpr int CB = GCfg<T>::kCb;
   constexpr int ROWS = kGWaves * CB * 32;
   __shared__ __attribute__((aligned(16))) T k_lds[2][kGKt * 64];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][64 * kGVld];
+  __shared__ __attribute__((aligned(16))) T v_lds[2][GLds<T>::kVElems];
 
   // workgroup -> (KV group, query tile), XCD-aware
   const int64_t bid = blockIdx.x;
@@ -135,11 +292,17 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   const T* ksg = A.ks + (int64_t)grp * A.m * 64;
   const T* vsg = A.vs + (int64_t)grp * A.m * 64;
 
-  // query fragments of this lane's columns
+  GStage<T> stage;
+  g_load<T>(stage, ksg, vsg, 0, A.m, tid);
+
+  // query fragments of this lane's columns, and their softmax references
   QFrag<T> qf[CB];
   int64_t tok[CB];
   int head[CB];
   bool valid[CB];
+  GCol st[CB];
+  const float kmax = A.kmax ? A.kmax[grp] : 0.0f;
+  bool all_fixed = true, all_zero = true;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int64_t row = tile * ROWS + (int64_t)(wave * CB + cb) * 32 + col;
@@ -147,108 +310,53 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
     tok[cb] = valid[cb] ? row / A.grp : 0;
     head[cb] = grp * A.grp + (valid[cb] ? (int)(row % A.grp) : 0);
     load_qfrag<T>(qf[cb], A.q + (tok[cb] * A.hq + head[cb]) * 64 + h * 32, valid[cb]);
+    st[cb].l = 0.0f;
+    st[cb].m = kNegInf;
+    st[cb].track = true;
+    if (A.kmax) {
+      float q2 = 0.0f;
+#pragma unroll
+      for (int s = 0; s < Mma<T>::kQkSteps; ++s) {
+        if constexpr (GLds<T>::kF32) {
+          q2 = fmaf(qf[cb].f[s], qf[cb].f[s], q2);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q2 = fmaf((float)qf[cb].f[s][e], (float)qf[cb].f[s][e], q2);
+        }
+      }
+      const float bound = sqrtf(pair_sum(q2)) * kmax * kBoundMargin;
+      if (bound <= kSafeBound) {
+        st[cb].track = false;
+        st[cb].m = fmaxf(bound - kRefHeadroom, 0.0f);
+      }
+    }
+    all_fixed = all_fixed && !st[cb].track;
+    all_zero = all_zero && !st[cb].track && st[cb].m == 0.0f;
   }
 
   f32x16 o[CB][2];
-  SoftmaxState sm[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     o[cb][0] = f32x16{};
     o[cb][1] = f32x16{};
-    sm[cb].m = kNegInf;
-    sm[cb].l = 0.0f;
   }
 
-  const int64_t nt = (A.m + kGKt - 1) / kGKt;
-  GStage<T> stage;
-  g_load<T>(stage, ksg, vsg, 0, A.m, tid);
-  for (int64_t t = 0; t < nt; ++t) {
-    const int b = (int)(t & 1);
-    g_store<T>(stage, k_lds[b], v_lds[b], tid);
-    __syncthreads();
-    if (t + 1 < nt) g_load<T>(stage, ksg, vsg, (t + 1) * kGKt, A.m, tid);
-
-    const T* kl = k_lds[b];
-    const T* vl = v_lds[b];
-    const int64_t k0 = t * kGKt;
-
-    f32x16 s[2][CB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      KFrag<T> kf;
-      load_kfrag<T>(kf, kl, kb * 32 + col, h);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) s[kb][cb] = qk_tile<T>(kf, qf[cb]);
-    }
-    if (k0 + kGKt > A.m) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = k0 + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (key >= A.m)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) s[kb][cb][v] = kNegInf;
-        }
-    }
-
-    typename Mma<T>::frag pf[2][CB][Mma<T>::kPvSteps];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][cb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = mx * A.c;
-      const bool upd = mt > sm[cb].m + kRescaleSlack;
-      if (__any(upd)) {
-        const float mn = upd ? mt : sm[cb].m;
-        const float alpha = upd ? __builtin_amdgcn_exp2f(sm[cb].m - mn) : 1.0f;
-        sm[cb].m = mn;
-        sm[cb].l *= alpha;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          o[cb][0][v] *= alpha;
-          o[cb][1][v] *= alpha;
-        }
-      }
-      const float mu = sm[cb].m == kNegInf ? 0.0f : sm[cb].m;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][cb][v], A.c, -mu));
-          s[kb][cb][v] = p;
-          sm[cb].l += p;
-        }
-#pragma unroll
-        for (int st = 0; st < Mma<T>::kPvSteps; ++st) pf[kb][cb][st] = Mma<T>::p_frag(s[kb][cb], st);
-      }
-    }
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        typename Mma<T>::frag vf[Mma<T>::kPvSteps];
-        v_frags<T>(vf, vl, db * 32 + col, kb * 32, h);
-#pragma unroll
-        for (int st = 0; st < Mma<T>::kPvSteps; ++st)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) o[cb][db] = Mma<T>::mma(vf[st], pf[kb][cb][st], o[cb][db]);
-      }
-  }
+  // one code path per wave; each query's arithmetic is the same in all of them
+  if (A.kmax && __all(all_zero))
+    g_stream<T, CB, kZeroRef>(k_lds, v_lds, stage, ksg, vsg, A, qf, st, o, tid, lane);
+  else if (A.kmax && __all(all_fixed))
+    g_stream<T, CB, kFixedRef>(k_lds, v_lds, stage, ksg, vsg, A, qf, st, o, tid, lane);
+  else
+    g_stream<T, CB, kGeneral>(k_lds, v_lds, stage, ksg, vsg, A, qf, st, o, tid, lane);
 
   // epilogue: normalise, write o_cmp or the gated output
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const float l = sm[cb].l + __shfl_xor(sm[cb].l, 32);
+    const float l = pair_sum(st[cb].l);
     if (!valid[cb]) continue;
     const float inv = 1.0f / l;
     const int64_t rbase = (tok[cb] * A.hq + head[cb]) * 64;
-    if (A.lse && h == 0) A.lse[tok[cb] * A.hq + head[cb]] = (sm[cb].m + __log2f(l)) * kLn2;
+    if (A.lse && h == 0) A.lse[tok[cb] * A.hq + head[cb]] = (st[cb].m + __log2f(l)) * kLn2;
     float g0 = 0.0f, g1 = 0.0f;
     if constexpr (kGate) {
       const float* gl = A.gate + (A.gate_per_head ? (tok[cb] * A.hq + head[cb]) * 2 : tok[cb] * 2);
@@ -268,7 +376,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
         for (int j = 0; j < 4; ++j) r[j] = o[cb][db][4 * q4 + j] * inv;
         if constexpr (kGate) {
           const f32x4 ol = *reinterpret_cast<const f32x4*>(A.o_loc + rbase + d0);
-          if constexpr (std::is_same<T, float>::value) {
+          if constexpr (GLds<T>::kF32) {
             f32x4 w;
 #pragma unroll
             for (int j = 0; j < 4; ++j) w[j] = g0 * ol[j] + g1 * r[j];
@@ -286,10 +394,31 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   }
 }
 
+// kmax[g] = max_j part[g][j] over nparts per-block summary norms.
+__global__ __launch_bounds__(1024) void k_kmax(const float* __restrict__ part, int64_t nparts,
+                                               float* kmax) {
+  __shared__ float red[1024];
+  const float* p = part + (int64_t)blockIdx.x * nparts;
+  float x = 0.0f;
+  for (int64_t i = threadIdx.x; i < nparts; i += blockDim.x) x = fmaxf(x, p[i]);
+  red[threadIdx.x] = x;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) kmax[blockIdx.x] = red[0];
+}
+
+hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, hipStream_t s) {
+  hipLaunchKernelGGL(k_kmax, dim3(g.Hkv), dim3(1024), 0, s, knorm, (int64_t)g.M, kmax);
+  return hipGetLastError();
+}
+
 template <typename T, bool kGate>
 static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const void* vs,
-                           int64_t m, float* o_cmp, float* lse, const float* o_loc,
-                           const float* gate, void* out, hipStream_t s) {
+                           int64_t m, float c, const float* kmax, float* o_cmp, float* lse,
+                           const float* o_loc, const float* gate, void* out, hipStream_t s) {
   constexpr int ROWS = kGWaves * GCfg<T>::kCb * 32;
   GArgs<T> A;
   A.q = (const T*)q;
@@ -300,12 +429,13 @@ static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const v
   A.hq = g.Hq;
   A.hkv = g.Hkv;
   A.grp = g.G;
-  A.c = g.scale * kLog2e;
+  A.c = c;
   A.o_cmp = o_cmp;
   A.lse = lse;
   A.o_loc = o_loc;
   A.gate = gate;
   A.out = (T*)out;
+  A.kmax = kmax;
   A.gate_per_head = g.gate_per_head;
   A.tiles = (g.N * g.G + ROWS - 1) / ROWS;
   int64_t blocks;
@@ -322,15 +452,21 @@ static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const v
 }
 
 hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
-                              const void* v_sum, int64_t m, float* o_cmp, float* lse,
-                              const float* o_loc, const float* gate, void* out,
+                              const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
+                              float* lse, const float* o_loc, const float* gate, void* out,
                               hipStream_t s) {
   const bool gated = o_cmp == nullptr;
+  // with kmax the summaries carry the softmax scale in log2 units already
+  const float c = kmax ? 1.0f : g.scale * kLog2e;
   if (g.bf16)
-    return gated ? launch_g<bf16_t, true>(g, q_rot, k_sum, v_sum, m, o_cmp, lse, o_loc, gate, out, s)
-                 : launch_g<bf16_t, false>(g, q_rot, k_sum, v_sum, m, o_cmp, lse, o_loc, gate, out, s);
-  return gated ? launch_g<float, true>(g, q_rot, k_sum, v_sum, m, o_cmp, lse, o_loc, gate, out, s)
-               : launch_g<float, false>(g, q_rot, k_sum, v_sum, m, o_cmp, lse, o_loc, gate, out, s);
+    return gated ? launch_g<bf16_t, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, o_loc,
+                                          gate, out, s)
+                 : launch_g<bf16_t, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse,
+                                           o_loc, gate, out, s);
+  return gated ? launch_g<float, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, o_loc,
+                                       gate, out, s)
+               : launch_g<float, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, o_loc,
+                                        gate, out, s);
 }
 
 }  // namespace pack3d

@@ -122,7 +122,7 @@ bool local_supported(const Geom& g) {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t q_rot, k_rot, k_sum, v_sum, o_loc, total;
+  size_t q_rot, k_rot, k_sum, v_sum, o_loc, knorm, kmax, total;
 };
 
 WsLayout ws_layout(const Geom& g) {
@@ -139,6 +139,10 @@ WsLayout ws_layout(const Geom& g) {
   off += align256((size_t)g.Hkv * g.M * 64 * es);
   w.o_loc = off;
   off += align256((size_t)g.N * g.Hq * 64 * 4);
+  w.knorm = off;
+  off += align256((size_t)g.Hkv * g.M * 4);
+  w.kmax = off;
+  off += align256((size_t)g.Hkv * 4);
   w.total = off;
   return w;
 }
@@ -184,8 +188,8 @@ int pack3d_block_summary(const pack3d_problem* prob, const void* k_cmp, const vo
   if (rc) return rc;
   if (!k_cmp || !v_cmp || !cell_to_pos || !k_sum || !v_sum)
     return fail(PACK3D_ERR_NULL, "pack3d_block_summary: NULL tensor argument");
-  return hip_status(launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
-                                         (hipStream_t)stream),
+  return hip_status(launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum, 1.0f,
+                                         nullptr, (hipStream_t)stream),
                     "k_block_summary");
 }
 
@@ -213,8 +217,8 @@ int pack3d_global_attn(const pack3d_problem* prob, const void* q_rot, const void
   if (!q_rot || !k_sum || !v_sum || !o_cmp)
     return fail(PACK3D_ERR_NULL, "pack3d_global_attn: NULL tensor argument");
   if (m < 1) return fail(PACK3D_ERR_SHAPE, "pack3d_global_attn: m = %d must be >= 1", m);
-  return hip_status(launch_global_attn(g, q_rot, k_sum, v_sum, m, o_cmp, lse_cmp, nullptr,
-                                       nullptr, nullptr, (hipStream_t)stream),
+  return hip_status(launch_global_attn(g, q_rot, k_sum, v_sum, m, nullptr, o_cmp, lse_cmp,
+                                       nullptr, nullptr, nullptr, (hipStream_t)stream),
                     "k_global_attn");
 }
 
@@ -255,15 +259,22 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
   void* k_sum = ws + w.k_sum;
   void* v_sum = ws + w.v_sum;
   float* o_loc = (float*)(ws + w.o_loc);
+  float* knorm = (float*)(ws + w.knorm);
+  float* kmax = (float*)(ws + w.kmax);
   hipError_t e;
   if ((e = launch_rope(g, q, q_rot, g.Hq, coords, s)) != hipSuccess) return hip_status(e, "k_rope(q)");
   if ((e = launch_rope(g, k_loc, k_rot, g.Hkv, coords, s)) != hipSuccess)
     return hip_status(e, "k_rope(k_loc)");
-  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum, s)) != hipSuccess)
+  // summaries scaled into log2-domain logits, with their norms for the
+  // softmax bound of the query->summary kernel
+  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
+                                g.scale * 1.4426950408889634f, knorm, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
+  if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
   if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, nullptr, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
-  e = launch_global_attn(g, q_rot, k_sum, v_sum, g.M, nullptr, nullptr, o_loc, gate_logits, out, s);
+  e = launch_global_attn(g, q_rot, k_sum, v_sum, g.M, kmax, nullptr, nullptr, o_loc, gate_logits,
+                         out, s);
   return hip_status(e, "k_global_attn(gated)");
 }
 

@@ -264,6 +264,30 @@ __device__ __forceinline__ f32x16 qk_tile(const KFrag<T>& k, const QFrag<T>& q) 
   return acc;
 }
 
+// Lanes l and l+32 hold the same MFMA column: combine their values.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of the 8 probabilities of a bf16 PV operand (as rounded for the MFMA).
+__device__ __forceinline__ float frag_sum(const bf16x8& f, float acc) {
+  const bf16x2 one = {(bf16_t)1.0f, (bf16_t)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {f[2 * i], f[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(float f, float acc) { return acc + f; }
+
 // Online-softmax state of one query column (per lane; lanes l and l+32 hold
 // the same column and always agree on m).
 struct SoftmaxState {

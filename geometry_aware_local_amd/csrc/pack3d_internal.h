@@ -40,17 +40,23 @@ struct Geom {
 // Launchers (each returns the launch status; no host synchronisation).
 hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
                        const int32_t* coords, hipStream_t s);
+// kscale multiplies the key summaries; knorm (nullable) receives their norms
+// [Hkv, M] after scaling.
 hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_cmp,
                                 const float* a, const int32_t* cell_to_pos, void* k_sum,
-                                void* v_sum, hipStream_t s);
+                                void* v_sum, float kscale, float* knorm, hipStream_t s);
+// kmax[g] = max over the M key-summary norms of group g.
+hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, hipStream_t s);
 hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot,
                              const void* v, const int32_t* cell_to_pos, float* o_loc,
                              float* lse, hipStream_t s);
 // o_cmp != nullptr: write o_cmp (fp32).  Otherwise gate-mix epilogue:
-// out = g_loc*o_loc + g_cmp*o_cmp in the problem dtype.
+// out = g_loc*o_loc + g_cmp*o_cmp in the problem dtype.  kmax != nullptr:
+// the key summaries are pre-scaled by scale*log2(e) and kmax[g] bounds their
+// norms (enables the fixed softmax reference); nullptr: unscaled summaries.
 hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
-                              const void* v_sum, int64_t m, float* o_cmp, float* lse,
-                              const float* o_loc, const float* gate, void* out,
+                              const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
+                              float* lse, const float* o_loc, const float* gate, void* out,
                               hipStream_t s);
 hipError_t launch_gate_mix(const Geom& g, const float* o_loc, const float* o_cmp,
                            const float* gate, void* out, hipStream_t s);

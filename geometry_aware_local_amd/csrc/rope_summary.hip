@@ -63,10 +63,14 @@ hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
 constexpr int kSumWaves = 4;
 constexpr int kMaxPasses = kMaxBlockVol / 8;
 
+// The forward asks for the key summaries multiplied by kscale (the softmax
+// scale in log2 units, applied once before the single rounding) and for the
+// norm of every scaled key summary in knorm [Hkv, M].
 template <typename T>
 __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
     const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ a,
-    const int32_t* __restrict__ c2p, T* __restrict__ ks, T* __restrict__ vs, Geom g) {
+    const int32_t* __restrict__ c2p, T* __restrict__ ks, T* __restrict__ vs, Geom g,
+    float kscale, float* __restrict__ knorm) {
   const int lane = threadIdx.x & 63;
   const int64_t j = (int64_t)blockIdx.x * kSumWaves + (threadIdx.x >> 6);
   if (j >= g.M) return;
@@ -121,25 +125,38 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
         av[i] += __shfl_xor(av[i], off);
       }
     }
+    float n2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ak[i] *= kscale;
+      n2 = fmaf(ak[i], ak[i], n2);
+    }
     if (slot == 0) {
       const int64_t o = ((int64_t)grp * g.M + j) * 64 + chunk * 8;
       store8<T>(ks + o, ak);
       store8<T>(vs + o, av);
+    }
+    if (knorm) {
+#pragma unroll
+      for (int off = 1; off < 8; off <<= 1) n2 += __shfl_xor(n2, off);
+      if (lane == 0) knorm[(int64_t)grp * g.M + j] = sqrtf(n2);
     }
   }
 }
 
 hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_cmp,
                                 const float* a, const int32_t* c2p, void* k_sum, void* v_sum,
-                                hipStream_t s) {
+                                float kscale, float* knorm, hipStream_t s) {
   const dim3 grid((unsigned)((g.M + kSumWaves - 1) / kSumWaves));
   const dim3 block(64 * kSumWaves);
   if (g.bf16)
     hipLaunchKernelGGL(k_block_summary<bf16_t>, grid, block, 0, s, (const bf16_t*)k_cmp,
-                       (const bf16_t*)v_cmp, a, c2p, (bf16_t*)k_sum, (bf16_t*)v_sum, g);
+                       (const bf16_t*)v_cmp, a, c2p, (bf16_t*)k_sum, (bf16_t*)v_sum, g, kscale,
+                       knorm);
   else
     hipLaunchKernelGGL(k_block_summary<float>, grid, block, 0, s, (const float*)k_cmp,
-                       (const float*)v_cmp, a, c2p, (float*)k_sum, (float*)v_sum, g);
+                       (const float*)v_cmp, a, c2p, (float*)k_sum, (float*)v_sum, g, kscale,
+                       knorm);
   return hipGetLastError();
 }
 

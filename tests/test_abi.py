@@ -104,11 +104,13 @@ def test_unsupported_group_ratio(pk):
 def test_workspace_size_matches_layout(pk):
     p = _prob(pk, grid=(64, 64, 64), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
     n, m = 64 ** 3, 64 ** 3 // 16
-    bf16 = 2 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) + 4 * n * 8 * 64
+    a256 = lambda b: (b + 255) // 256 * 256
+    fp32_parts = 4 * n * 8 * 64 + a256(4 * 2 * m) + a256(4 * 2)   # o_loc, summary norms, kmax
+    bf16 = 2 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) + fp32_parts
     assert pk.pack3d_forward_workspace_size(p) == bf16
     p.dtype = 0
     assert pk.pack3d_forward_workspace_size(p) == 4 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) \
-        + 4 * n * 8 * 64
+        + fp32_parts
 
 
 def test_error_string_is_per_call(pk):
