@@ -108,13 +108,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="block_bf16_64x64x64", choices=sorted(sg.WORKLOADS))
-    ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense", action="store_true",
                     help="also time dense axial-RoPE attention (1x1x1 blocks) on the same inputs")
     ap.add_argument("--profile-only", action="store_true",
-                    help="for counter runs: a known-size copy probe, then each kernel 3 times")
+                    help="for counter runs: a known-size copy probe, then 3 forwards")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the operator's "
@@ -141,92 +140,78 @@ def main() -> int:
     ws = pk.alloc_workspace(prob, q.device)
     out = torch.empty_like(q)
     n = w.n_tokens
-
-    def forward():
-        pk.pack3d_forward(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, c2p, gate,
-                          workspace=ws, out=out)
-
-    # split-op buffers (the same kernels the forward launches)
-    q_rot, k_rot = torch.empty_like(q), torch.empty_like(k_loc)
-
-    def split_ops():
-        return {
-            "k_rope": lambda: pk.pack3d_rope(prob, q, coords, out=q_rot),
-            "k_block_summary": lambda: pk.pack3d_block_summary(prob, k_cmp, v_cmp, a, c2p),
-            "k_local_attn": lambda: pk.pack3d_local_attn(prob, q_rot, k_rot, v_loc, c2p),
-            "k_global_attn": lambda: pk.pack3d_global_attn(prob, q_rot, ks, vs),
-        }
-
-    pk.pack3d_rope(prob, k_loc, coords, out=k_rot)
-    ks, vs = pk.pack3d_block_summary(prob, k_cmp, v_cmp, a, c2p)
+    fargs = (prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, c2p, gate)
 
     if args.profile_only:
         x = torch.empty(64 << 20, dtype=torch.float32, device="cuda")    # 256 MiB
         y = torch.empty_like(x)
         for _ in range(3):
             torch.neg(x, out=y)           # copy probe: reads and writes 256 MiB
-        ops = split_ops()
-        for name in ("k_rope", "k_block_summary", "k_local_attn", "k_global_attn"):
-            for _ in range(3):
-                ops[name]()
-        forward()
+        for _ in range(3):
+            pk.pack3d_forward(*fargs, workspace=ws, out=out)
         torch.cuda.synchronize()
         print("[bench] profile-only run done", file=sys.stderr, flush=True)
         return 0
 
     for _ in range(args.warmup):
-        forward()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pk.pack3d_forward(*fargs, workspace=ws, out=out)
+    # timed region: every step records an event before and after each stage,
+    # on the stream the kernels run on
+    nev = pk.PACK3D_FORWARD_STAGES + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+              for _ in range(args.steps)]
+    for evs in events:
+        for e in evs:
+            e.record()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        forward()
-    e1.record()
+    for evs in events:
+        pk.pack3d_forward_timed(*fargs, evs, workspace=ws, out=out)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] forward {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f})",
-          file=sys.stderr, flush=True)
+    ms = events[0][0].elapsed_time(events[-1][-1]) / args.steps
+    stage_ms = [sum(evs[i].elapsed_time(evs[i + 1]) for evs in events) / args.steps
+                for i in range(nev - 1)]
+    stages = dict(zip(pk.FORWARD_STAGE_NAMES, stage_ms))
+    print(f"[bench] forward {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); " +
+          ", ".join(f"{k} {v:.3f}" for k, v in stages.items()), file=sys.stderr, flush=True)
 
-    # per-kernel times: each split op launched back to back, HIP events on the
-    # current stream (the stream the binding launches on)
-    kern = {}
-    for name, fn in split_ops().items():
-        fn()
-        torch.cuda.synchronize()
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record()
-        for _ in range(args.kernel_reps):
-            fn()
-        b1.record()
-        torch.cuda.synchronize()
-        kern[name] = b0.elapsed_time(b1) / args.kernel_reps
     work = algorithmic(w)
-    peak_mfma = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    g_tflops = work["global_flops"] / (kern["k_global_attn"] * 1e-3) / 1e12
     es = 2 if w.dtype == "bf16" else 4
-    rope_q_bytes = 2 * n * w.n_q_heads * 64 * es + n * 12     # the timed op rotates Q only
+    peak_mfma = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    rope_q = 2 * n * w.n_q_heads * 64 * es + n * 12
+    rope_k = 2 * n * w.n_kv_heads * 64 * es + n * 12
+    # the forward's summary stage also writes the key-summary norms
+    summary = work["summary_bytes"] + w.n_kv_heads * w.n_blocks * 4
+    gbs = lambda b, t: b / (t * 1e-3) / 1e9
+    tfl = lambda f, t: f / (t * 1e-3) / 1e12
     kernels = {
-        "k_rope": {"ms": kern["k_rope"], "bound": "hbm",
-                   "gbs": rope_q_bytes / (kern["k_rope"] * 1e-3) / 1e9},
-        "k_block_summary": {"ms": kern["k_block_summary"], "bound": "hbm",
-                            "gbs": work["summary_bytes"] / (kern["k_block_summary"] * 1e-3) / 1e9},
-        "k_local_attn": {"ms": kern["k_local_attn"], "bound": "mfma",
-                         "tflops": work["local_flops"] / (kern["k_local_attn"] * 1e-3) / 1e12},
-        "k_global_attn": {"ms": kern["k_global_attn"], "bound": "mfma", "tflops": g_tflops},
+        "k_rope(q)": {"ms": stages["k_rope(q)"], "bound": "hbm",
+                      "gbs": gbs(rope_q, stages["k_rope(q)"])},
+        "k_rope(k_loc)": {"ms": stages["k_rope(k_loc)"], "bound": "hbm",
+                          "gbs": gbs(rope_k, stages["k_rope(k_loc)"])},
+        "k_block_summary": {"ms": stages["k_block_summary"], "bound": "hbm",
+                            "gbs": gbs(summary, stages["k_block_summary"])},
+        "k_kmax": {"ms": stages["k_kmax"], "bound": "launch"},
+        "k_local_attn": {"ms": stages["k_local_attn"], "bound": "mfma",
+                         "tflops": tfl(work["local_flops"], stages["k_local_attn"])},
+        "k_global_attn(gated)": {"ms": stages["k_global_attn(gated)"], "bound": "mfma",
+                                 "tflops": tfl(work["global_flops"],
+                                               stages["k_global_attn(gated)"])},
     }
     for v in kernels.values():
         if v["bound"] == "hbm":
             v["frac"] = v["gbs"] / HBM_PEAK_GBS
-        else:
+        elif v["bound"] == "mfma":
             v["frac"] = v["tflops"] / peak_mfma
+    g_tflops = kernels["k_global_attn(gated)"]["tflops"]
 
     extra = {}
     if args.dense:
+        # dense axial-RoPE attention on the same inputs: 1x1x1 blocks, a = 1
         dprob = pk.make_problem(w.grid, w.n_q_heads, w.n_kv_heads, w.window, (1, 1, 1), dt,
                                 w.rope_pairs, w.rope_base)
+        q_rot = pk.pack3d_rope(prob, q, coords)
         dk, dv = pk.pack3d_block_summary(dprob, k_cmp, v_cmp, None, c2p)
         pk.pack3d_global_attn(dprob, q_rot, dk, dv)
         torch.cuda.synchronize()
@@ -238,8 +223,7 @@ def main() -> int:
         dms = b0.elapsed_time(b1)
         dfl = 4 * n * w.n_q_heads * n * 64
         extra["dense_companion"] = {
-            "ms": dms, "tflops": dfl / (dms * 1e-3) / 1e12,
-            "frac": dfl / (dms * 1e-3) / 1e12 / peak_mfma,
+            "ms": dms, "tflops": tfl(dfl, dms), "frac": tfl(dfl, dms) / peak_mfma,
             "speedup_pack3d_vs_dense": dms / ms}
 
     cpu = None
@@ -264,7 +248,7 @@ def main() -> int:
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 64,
                    "window": list(w.window), "block": list(w.block), "summaries": w.n_blocks,
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "kernel": "k_global_attn",
+        "roofline": {"bound": "mfma", "kernel": "k_global_attn (gated, in the forward)",
                      "achieved": g_tflops, "peak": peak_mfma, "unit": "TFLOP/s",
                      "frac": g_tflops / peak_mfma, "traffic": measured_traffic()},
         "cpu_baseline": cpu,

@@ -233,10 +233,16 @@ int pack3d_gate_mix(const pack3d_problem* prob, const float* o_loc, const float*
                     "k_gate_mix");
 }
 
-int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
-                   const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
-                   const int32_t* coords, const int32_t* cell_to_pos, const float* gate_logits,
-                   void* out, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward's launch sequence; with `ev` (PACK3D_FORWARD_STAGES + 1 events)
+// an event is recorded on the stream before the first stage and after each.
+int forward_impl(const pack3d_problem* prob, const void* q, const void* k_loc, const void* v_loc,
+                 const void* k_cmp, const void* v_cmp, const float* a, const int32_t* coords,
+                 const int32_t* cell_to_pos, const float* gate_logits, void* out,
+                 void* workspace, size_t ws_bytes, void* stream, void* const* ev, int32_t nev) {
   Geom g;
   int rc = make_geom(prob, &g);
   if (rc) return rc;
@@ -252,6 +258,13 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
                 w.total);
   if ((uintptr_t)workspace & 255)
     return fail(PACK3D_ERR_WORKSPACE, "pack3d_forward: workspace not 256-byte aligned");
+  if (ev) {
+    if (nev != PACK3D_FORWARD_STAGES + 1)
+      return fail(PACK3D_ERR_SHAPE, "pack3d_forward_timed: %d events, need %d", nev,
+                  PACK3D_FORWARD_STAGES + 1);
+    for (int i = 0; i < nev; ++i)
+      if (!ev[i]) return fail(PACK3D_ERR_NULL, "pack3d_forward_timed: event %d is NULL", i);
+  }
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   void* q_rot = ws + w.q_rot;
@@ -261,21 +274,55 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
   float* o_loc = (float*)(ws + w.o_loc);
   float* knorm = (float*)(ws + w.knorm);
   float* kmax = (float*)(ws + w.kmax);
+  int stage = 0;
+  auto mark = [&]() -> hipError_t {
+    return ev ? hipEventRecord((hipEvent_t)ev[stage++], s) : hipSuccess;
+  };
   hipError_t e;
+  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   if ((e = launch_rope(g, q, q_rot, g.Hq, coords, s)) != hipSuccess) return hip_status(e, "k_rope(q)");
+  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   if ((e = launch_rope(g, k_loc, k_rot, g.Hkv, coords, s)) != hipSuccess)
     return hip_status(e, "k_rope(k_loc)");
+  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   // summaries scaled into log2-domain logits, with their norms for the
   // softmax bound of the query->summary kernel
   if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
                                 g.scale * 1.4426950408889634f, knorm, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
+  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
+  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, nullptr, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
+  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   e = launch_global_attn(g, q_rot, k_sum, v_sum, g.M, kmax, nullptr, nullptr, o_loc, gate_logits,
                          out, s);
-  return hip_status(e, "k_global_attn(gated)");
+  if (e != hipSuccess) return hip_status(e, "k_global_attn(gated)");
+  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
+                   const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                   const int32_t* coords, const int32_t* cell_to_pos, const float* gate_logits,
+                   void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits,
+                      out, workspace, ws_bytes, stream, nullptr, 0);
+}
+
+int pack3d_forward_timed(const pack3d_problem* prob, const void* q, const void* k_loc,
+                         const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                         const int32_t* coords, const int32_t* cell_to_pos,
+                         const float* gate_logits, void* out, void* workspace, size_t ws_bytes,
+                         void* stream, void* const* events, int32_t n_events) {
+  if (!events) return fail(PACK3D_ERR_NULL, "pack3d_forward_timed: events is NULL");
+  return forward_impl(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits,
+                      out, workspace, ws_bytes, stream, events, n_events);
 }
 
 int pack3d_build_cell_index(const pack3d_problem* prob, const int32_t* coords,

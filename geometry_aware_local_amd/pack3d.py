@@ -28,12 +28,15 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpack3d.so")
 
 PACK3D_F32, PACK3D_BF16 = 0, 1
+PACK3D_FORWARD_STAGES = 6
+FORWARD_STAGE_NAMES = ("k_rope(q)", "k_rope(k_loc)", "k_block_summary", "k_kmax", "k_local_attn",
+                       "k_global_attn(gated)")
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_UNSUPPORTED", -4: "ERR_WORKSPACE",
           -5: "ERR_PACKING", -6: "ERR_HIP"}
 
 EXPORTS = (
     "pack3d_rope", "pack3d_block_summary", "pack3d_local_attn", "pack3d_global_attn",
-    "pack3d_gate_mix", "pack3d_forward", "pack3d_forward_workspace_size",
+    "pack3d_gate_mix", "pack3d_forward", "pack3d_forward_timed", "pack3d_forward_workspace_size",
     "pack3d_build_cell_index", "pack3d_check_packing", "pack3d_last_error",
     "pack3d_backend_info", "pack3d_version",
 )
@@ -87,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "pack3d_global_attn": [P, V, V, V, I32, V, V, V],
         "pack3d_gate_mix": [P, V, V, V, V, V],
         "pack3d_forward": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V],
+        "pack3d_forward_timed": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V,
+                                 ctypes.POINTER(ctypes.c_void_p), I32],
         "pack3d_build_cell_index": [P, V, V, V],
         "pack3d_check_packing": [P, V, V, V, V],
     }
@@ -249,22 +254,47 @@ def alloc_workspace(prob: Problem, device) -> torch.Tensor:
     return torch.empty(size, dtype=torch.uint8, device=device)
 
 
-def pack3d_forward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
-                   workspace: Optional[torch.Tensor] = None,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The whole forward: out [N, Hq, 64] in the input dtype."""
+def _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
+                  workspace, out):
     n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
     gshape = (n, hq, 2) if prob.gate_per_head else (n, 2)
     ws = alloc_workspace(prob, q.device) if workspace is None else workspace
     out = _empty((n, hq, 64), dt, q) if out is None else out
-    _check(LIB.pack3d_forward(
-        ctypes.byref(prob), _ptr(q, dt, (n, hq, 64), "q"), _ptr(k_loc, dt, (n, hkv, 64), "k_loc"),
-        _ptr(v_loc, dt, (n, hkv, 64), "v_loc"), _ptr(k_cmp, dt, (n, hkv, 64), "k_cmp"),
-        _ptr(v_cmp, dt, (n, hkv, 64), "v_cmp"), _ptr(a, torch.float32, (n, hkv), "a"),
-        _ptr(coords, torch.int32, (n, 3), "coords"),
-        _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
-        _ptr(gate, torch.float32, gshape, "gate"), _ptr(out, dt, (n, hq, 64), "out"),
-        ws.data_ptr(), ws.numel(), _stream(q.device)))
+    args = (ctypes.byref(prob), _ptr(q, dt, (n, hq, 64), "q"),
+            _ptr(k_loc, dt, (n, hkv, 64), "k_loc"), _ptr(v_loc, dt, (n, hkv, 64), "v_loc"),
+            _ptr(k_cmp, dt, (n, hkv, 64), "k_cmp"), _ptr(v_cmp, dt, (n, hkv, 64), "v_cmp"),
+            _ptr(a, torch.float32, (n, hkv), "a"), _ptr(coords, torch.int32, (n, 3), "coords"),
+            _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
+            _ptr(gate, torch.float32, gshape, "gate"), _ptr(out, dt, (n, hq, 64), "out"),
+            ws.data_ptr(), ws.numel(), _stream(q.device))
+    return args, out
+
+
+def pack3d_forward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
+                   workspace: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole forward: out [N, Hq, 64] in the input dtype."""
+    args, out = _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
+                              workspace, out)
+    _check(LIB.pack3d_forward(*args))
+    return out
+
+
+def pack3d_forward_timed(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos,
+                         gate, events, workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pack3d_forward recording ``events`` (PACK3D_FORWARD_STAGES + 1 timing
+    torch.cuda.Event objects) around its stages; stage i lasts
+    ``events[i].elapsed_time(events[i + 1])`` ms."""
+    if len(events) != PACK3D_FORWARD_STAGES + 1:
+        raise ValueError(f"need {PACK3D_FORWARD_STAGES + 1} events")
+    for e in events:          # torch creates the HIP event at its first record
+        if not e.cuda_event:
+            e.record()
+    handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    args, out = _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
+                              workspace, out)
+    _check(LIB.pack3d_forward_timed(*args, handles, len(events)))
     return out
 
 

@@ -61,8 +61,9 @@ typedef enum pack3d_dtype { PACK3D_F32 = 0, PACK3D_BF16 = 1 } pack3d_dtype;
 /*
  * One operator instance.
  *   grid[3]        lattice extents Z, Y, X (all >= 1); N = Z*Y*X < 2^31.
- *   n_q_heads      Hq; n_kv_heads Hkv; Hq % Hkv == 0 and Hq/Hkv in
- *                  {1,2,4,8,16,32} (query heads h read KV group h/(Hq/Hkv)).
+ *   n_q_heads      Hq; n_kv_heads Hkv; Hq % Hkv == 0 (query head h reads KV
+ *                  group h/(Hq/Hkv)); the local branch and the forward take
+ *                  Hq/Hkv in {1,2,4,8,16}.
  *   head_dim       d_h; only 64 is supported.
  *   window[3]      odd extents of the local box (notes, key design 3: the
  *                  neighbourhood is a coordinate box); supported up to 3x7x7.
@@ -169,6 +170,24 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
                    const int32_t* coords, const int32_t* cell_to_pos,
                    const float* gate_logits, void* out, void* workspace, size_t ws_bytes,
                    void* stream);
+
+/*
+ * pack3d_forward with per-stage timing: the same launches, plus an event
+ * recorded on `stream` before the first stage and after each of the
+ * PACK3D_FORWARD_STAGES stages, in this order:
+ *   0 RoPE of q, 1 RoPE of k_loc, 2 block summaries (keys pre-scaled into
+ *   log2-domain logits, with their norms), 3 per-group max summary norm,
+ *   4 local attention, 5 query->summary attention with the gate.
+ * events: PACK3D_FORWARD_STAGES + 1 hipEvent_t handles created by the caller
+ * (timing enabled); n_events must equal that count.  The elapsed time
+ * between events i and i+1 is stage i.  Errors as pack3d_forward.
+ */
+#define PACK3D_FORWARD_STAGES 6
+int pack3d_forward_timed(const pack3d_problem* prob, const void* q, const void* k_loc,
+                         const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                         const int32_t* coords, const int32_t* cell_to_pos,
+                         const float* gate_logits, void* out, void* workspace, size_t ws_bytes,
+                         void* stream, void* const* events, int32_t n_events);
 
 /* Bytes of workspace pack3d_forward needs for this problem (0 if invalid). */
 size_t pack3d_forward_workspace_size(const pack3d_problem* prob);

@@ -386,3 +386,25 @@ def test_workspace_too_small_is_rejected(pk):
     with pytest.raises(pk.Pack3DError, match="ERR_WORKSPACE"):
         pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"],
                           d["coords"], d["cell_to_pos"], d["gate"], workspace=ws)
+
+
+def test_forward_timed_matches_forward(pk):
+    """The per-stage timed forward launches the same kernels: bitwise equal
+    output, and its stage times add up to the whole."""
+    w = MORTON.with_(grid=(8, 32, 32))
+    _say("forward_timed", w.name)
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    args = (prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"], d["coords"],
+            d["cell_to_pos"], d["gate"])
+    ref = pk.pack3d_forward(*args)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(pk.PACK3D_FORWARD_STAGES + 1)]
+    out = pk.pack3d_forward_timed(*args, ev)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    stages = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    assert all(t >= 0 for t in stages)
+    assert abs(sum(stages) - ev[0].elapsed_time(ev[-1])) < 1e-3
+    with pytest.raises(ValueError):
+        pk.pack3d_forward_timed(*args, ev[:-1])
