@@ -301,6 +301,8 @@ static hipError_t launch_lt(const Geom& g, const void* q, const void* k, const v
 
 hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot, const void* v,
                              const int32_t* c2p, float* o_loc, float* lse, hipStream_t s) {
+  if (g.bf16 && local_bf16_serves(g.G))
+    return launch_local_attn_bf16(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
   if (g.bf16) return launch_lt<bf16_t>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
   return launch_lt<float>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
 }

@@ -1,0 +1,350 @@
+// Exact local-neighbourhood attention, bf16 kernel for query-group sizes
+// G = Hq/Hkv of 4, 8 and 16.
+//
+// "Geometry Matters in Packed 3D Attention", papernotes.org notes, key
+// design 3: the neighbourhood N(i) is a box of lattice coordinates, local K/V
+// tiles are streamed through on-chip memory, and no gathered neighbour
+// tensor is ever materialised.
+//
+// A workgroup owns a 1 x TY x TX tile of query cells of one z-plane and one
+// KV group, split into patches of 32/G cells (two cells wide); a patch's
+// (cell, head) pairs are the 32 columns of an MFMA block, so the G heads of
+// the group share every key fragment.  For every z-plane of the window the
+// workgroup copies the rotated K and the V rows of the tile plus a 3-cell
+// halo into LDS, gathering rows through cell_to_pos (by coordinate) with
+// asynchronous global->LDS copies, double-buffered so the next plane's
+// copies are in flight while this plane is computed.  A patch treats the
+// union of its cells' windows in that plane, for the largest supported
+// radius, as a dense 8-wide key set (so all shapes are compile-time):
+// S^T = K Q^T and O^T += V^T P^T on 32x32x16 bf16 MFMA, V^T read from the
+// row-major tile with the transposing LDS load.  Keys outside a query's
+// window or outside the lattice are masked to -inf and an online softmax
+// carries the state across planes.  Every reduction order is fixed by
+// coordinates, never by packing.
+#include "pack3d_device.h"
+
+namespace pack3d {
+
+namespace lb {
+
+constexpr int kHalo = 3;     // largest supported y/x radius
+constexpr int kKx = 8;       // key slots per row: patch width 2 + 2 * halo
+
+template <int G> struct Shape;   // patch PY x 2 cells, tile TY x TX cells
+template <> struct Shape<4> { static constexpr int PY = 4, TY = 8, TX = 8; };
+template <> struct Shape<8> { static constexpr int PY = 2, TY = 8, TX = 4; };
+template <> struct Shape<16> { static constexpr int PY = 1, TY = 4, TX = 4; };
+
+template <int G>
+struct Cfg {
+  static constexpr int PY = Shape<G>::PY, PX = 2, TY = Shape<G>::TY, TX = Shape<G>::TX;
+  static constexpr int KY = PY + 2 * kHalo;                 // key rows per plane
+  static constexpr int NKB = (KY * kKx + 31) / 32;          // 32-key blocks per plane
+  static constexpr int RX = TX - PX + kKx;                  // region width (cells)
+  static constexpr int RY = TY + 2 * kHalo;
+  static constexpr int RC = RX * RY;                        // region cells
+  static constexpr int RCP = (RC + 7) / 8 * 8;              // padded to 1 KB pieces
+  // key blocks round a patch's key rows up to 4*NKB: the last patch row
+  // reaches region row TY - PY + 4*NKB - 1, so the slot holds that many rows
+  // (the rows past RY are zero, never copied, and always masked)
+  static constexpr int RYA = TY - PY + 4 * NKB > RY ? TY - PY + 4 * NKB : RY;
+  static constexpr int RCA = RYA * RX > RCP ? RYA * RX : RCP;   // cells per slot
+  static constexpr int W = TY * TX / (PY * PX);             // waves = patches
+  static_assert(PY * PX * G == 32, "a patch is one MFMA column block");
+  static_assert(W <= 16, "at most 1024 threads");
+  static_assert(NKB * 4 >= KY, "key rows fit the key blocks");
+  // a key block is 4 region rows: keeps the K swizzle of a lane's row
+  static_assert((4 * RX) % 8 == 0, "block stride keeps the K swizzle");
+};
+
+struct Args {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const int32_t* c2p;
+  float* o;
+  float* lse;
+  int32_t Z, Y, X, hq, hkv;
+  int32_t rz, ry, rx;
+  float c;                 // scale * log2(e)
+  int32_t tiles_y, tiles_x;
+  int64_t nblocks;
+  int64_t per_xcd;
+};
+
+// 16-byte chunk positions in a 128-byte LDS row: K spreads 8 consecutive
+// rows over all banks for the MFMA A operand; V spreads 4 consecutive rows
+// for the transposing reads.
+__device__ __forceinline__ int k_swz(int cell, int chunk) { return chunk ^ (cell & 7); }
+__device__ __forceinline__ int v_swz(int cell, int chunk) { return chunk ^ ((2 * cell) & 6); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int G>
+__global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
+  using C = Cfg<G>;
+  constexpr int PY = C::PY, PX = C::PX, TX = C::TX, NKB = C::NKB, KY = C::KY, RX = C::RX,
+                RC = C::RC, RCP = C::RCP, RCA = C::RCA, W = C::W, NT = 64 * W;
+  // two plane slots, as separate arrays so copies into one are known not to
+  // alias reads of the other
+  __shared__ __attribute__((aligned(16))) bf16_t k_lds0[RCA * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t k_lds1[RCA * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t v_lds0[RCA * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t v_lds1[RCA * 64];
+
+  // workgroup -> (group, z, tile y, tile x); each XCD takes a contiguous range
+  const int64_t bid = blockIdx.x;
+  const int64_t lin = (bid % kNumXcd) * A.per_xcd + bid / kNumXcd;
+  if (lin >= A.nblocks) return;
+  const int tx = (int)(lin % A.tiles_x);
+  const int ty = (int)((lin / A.tiles_x) % A.tiles_y);
+  const int z0 = (int)((lin / ((int64_t)A.tiles_x * A.tiles_y)) % A.Z);
+  const int grp = (int)(lin / ((int64_t)A.tiles_x * A.tiles_y * A.Z));
+  const int y0 = ty * C::TY, x0 = tx * TX;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int hh = col % G, cip = col / G, qy = cip / PX, qx = cip % PX;
+  const int py0 = (wave / (TX / PX)) * PY, px0 = (wave % (TX / PX)) * PX;
+
+  // Region cells are copied in 1 KB pieces (8 cells): wave w owns pieces
+  // w, w + W, ...; lane l of a piece fills cell 8*piece + l/8 at chunk
+  // position l%8, which holds data chunk swz(cell, l%8) (the swizzles are
+  // involutions).  The packed positions of a plane's cells are gathered
+  // into registers one plane ahead of its copies.
+  constexpr int NPC = (RCP / 8 + W - 1) / W;   // pieces per wave
+  auto load_pos = [&](int zz, int32_t (&pos)[NPC]) {
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int cell = (wave + W * i) * 8 + (lane >> 3);
+      const int yy = y0 - kHalo + cell / RX, xx = x0 - kHalo + cell % RX;
+      // off the lattice (or past the region): token 0, finite and masked
+      pos[i] = cell < RC && yy >= 0 && yy < A.Y && xx >= 0 && xx < A.X
+                   ? A.c2p[((int64_t)zz * A.Y + yy) * A.X + xx]
+                   : 0;
+    }
+  };
+  const bf16_t* kg = A.k + (int64_t)grp * 64;
+  const bf16_t* vg = A.v + (int64_t)grp * 64;
+  const int64_t rstride = (int64_t)A.hkv * 64;
+  auto issue_loads = [&](const int32_t (&pos)[NPC], bf16_t* kl, bf16_t* vl) {
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      const int pc = wave + W * i;
+      if (pc < RCP / 8) {
+        const int cell = pc * 8 + (lane >> 3), cp = lane & 7;
+        const int64_t row = (int64_t)pos[i] * rstride;
+        __builtin_amdgcn_global_load_lds((const void*)(kg + row + k_swz(cell, cp) * 8),
+                                         (lds_ptr)(kl + pc * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vg + row + v_swz(cell, cp) * 8),
+                                         (lds_ptr)(vl + pc * 512), 16, 0, 0);
+      }
+    }
+  };
+
+  // this lane's query column
+  const int yq = y0 + py0 + qy, xq = x0 + px0 + qx;
+  const bool qok = yq < A.Y && xq < A.X;
+  const int64_t qpos = qok ? (int64_t)A.c2p[((int64_t)z0 * A.Y + yq) * A.X + xq] : -1;
+  QFrag<bf16_t> qf;
+  load_qfrag<bf16_t>(qf, A.q + (qpos * A.hq + grp * G + hh) * 64 + h * 32, qok);
+
+  // Window mask.  Key slot s of the patch is region cell (py0 + s/8, px0 +
+  // s%8); accumulator element e of 32-key block kb on lane half h is slot
+  // kb*32 + 8*(e/4) + 4h + e%4, i.e. key row 4kb + e/4 and key column
+  // 4h + e%4.  The key is valid iff its row and its column are.
+  bool rv[NKB * 4], cv[4];
+#pragma unroll
+  for (int r = 0; r < NKB * 4; ++r) {
+    const int dy = r - kHalo - qy, yk = y0 + py0 + r - kHalo;
+    rv[r] = r < KY && dy >= -A.ry && dy <= A.ry && yk >= 0 && yk < A.Y;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int kx = 4 * h + c, dx = kx - kHalo - qx, xk = x0 + px0 + kx - kHalo;
+    cv[c] = dx >= -A.rx && dx <= A.rx && xk >= 0 && xk < A.X;
+  }
+
+  f32x16 o0 = {}, o1 = {};
+  SoftmaxState sm;
+  sm.m = kNegInf;
+  sm.l = 0.0f;
+
+  // LDS element offsets of this lane's operand rows within a slot
+  const int kcell = (py0 + col / 8) * RX + px0 + col % 8;   // + 4*RX cells per key block
+  int koff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) koff[st] = kcell * 64 + k_swz(kcell, h * 4 + st) * 8;
+  const int r4 = lane & 15;
+  int voff[2][2];   // [half][dim block]; + (4*kb + 2t)*RX cells per PV step
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int cell = (py0 + half) * RX + px0 + 4 * h + (r4 >> 2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int dim = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (r4 & 3);
+      voff[half][db] = cell * 64 + v_swz(cell, dim >> 3) * 8 + (dim & 7);
+    }
+  }
+
+  auto compute_plane = [&](const bf16_t* kl, const bf16_t* vl) {
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      KFrag<bf16_t> kf;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        kf.f[st] = *reinterpret_cast<const bf16x8*>(kl + 4 * RX * 64 * kb + koff[st]);
+      s[kb] = qk_tile<bf16_t>(kf, qf);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!(rv[4 * kb + e / 4] && cv[e % 4])) s[kb][e] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    const float mt = pair_max(mx) * A.c;
+    const bool upd = mt > sm.m + kRescaleSlack;
+    if (__any(upd)) {
+      const float mn = upd ? mt : sm.m;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(sm.m - mn) : 1.0f;
+      sm.m = mn;
+      sm.l *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        o0[e] *= alpha;
+        o1[e] *= alpha;
+      }
+    }
+    const float mu = sm.m == kNegInf ? 0.0f : sm.m;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (4 * kb + 2 * t >= KY) continue;   // both key rows are padding: P = 0
+        f32x16 pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pr[8 * t + e] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + e], A.c, -mu));
+        const bf16x8 pf = Mma<bf16_t>::p_frag(pr, t);
+        sm.l = frag_sum(pf, sm.l);
+        const bf16_t* vrows = vl + (4 * kb + 2 * t) * RX * 64;
+        bf16x8 vf[2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const bf16x4 part = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(
+                    (__attribute__((address_space(3))) bf16_t*)(vrows + voff[half][db])));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vf[db][4 * half + j] = part[j];
+          }
+        o0 = Mma<bf16_t>::mma(vf[0], pf, o0);
+        o1 = Mma<bf16_t>::mma(vf[1], pf, o1);
+      }
+    }
+  };
+
+  // planes of the window inside the lattice (z0 itself always is)
+  const int zlo = z0 - A.rz < 0 ? 0 : z0 - A.rz;
+  const int zhi = z0 + A.rz >= A.Z ? A.Z - 1 : z0 + A.rz;
+  const int np = zhi - zlo + 1;
+
+  // zero the rows past the copied region once (they stay untouched)
+  for (int i = RCP * 8 + tid; i < RCA * 8; i += NT) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    st16(k_lds0 + 8 * i, z);
+    st16(k_lds1 + 8 * i, z);
+    st16(v_lds0 + 8 * i, z);
+    st16(v_lds1 + 8 * i, z);
+  }
+  int32_t pos_a[NPC], pos_b[NPC];   // positions of the next two planes
+  load_pos(zlo, pos_a);
+  __builtin_amdgcn_s_waitcnt(0);
+  issue_loads(pos_a, k_lds0, v_lds0);
+  if (np > 1) load_pos(zlo + 1, pos_a);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // plane p lives in slot p & 1; while it is computed the next plane's copies
+  // are in flight into the other slot and the positions of plane p + 2 are
+  // being gathered
+  for (int p = 0; p < np; p += 2) {
+    if (p + 1 < np) issue_loads(pos_a, k_lds1, v_lds1);
+    if (p + 2 < np) load_pos(zlo + p + 2, pos_b);
+    compute_plane(k_lds0, v_lds0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (p + 1 >= np) break;
+    if (p + 2 < np) issue_loads(pos_b, k_lds0, v_lds0);
+    if (p + 3 < np) load_pos(zlo + p + 3, pos_a);
+    compute_plane(k_lds1, v_lds1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  const float l = pair_sum(sm.l);
+  if (qpos < 0) return;
+  const float inv = 1.0f / l;
+  const int head = grp * G + hh;
+  const int64_t rbase = (qpos * A.hq + head) * 64;
+  if (A.lse && h == 0) A.lse[qpos * A.hq + head] = (sm.m + __log2f(l)) * kLn2;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    f32x4 r0, r1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r0[j] = o0[4 * q4 + j] * inv;
+      r1[j] = o1[4 * q4 + j] * inv;
+    }
+    *reinterpret_cast<f32x4*>(A.o + rbase + 8 * q4 + 4 * h) = r0;
+    *reinterpret_cast<f32x4*>(A.o + rbase + 32 + 8 * q4 + 4 * h) = r1;
+  }
+}
+
+template <int G>
+hipError_t launch(const Geom& g, const void* q, const void* k, const void* v, const int32_t* c2p,
+                  float* o, float* lse, hipStream_t s) {
+  using C = Cfg<G>;
+  Args A;
+  A.q = (const bf16_t*)q;
+  A.k = (const bf16_t*)k;
+  A.v = (const bf16_t*)v;
+  A.c2p = c2p;
+  A.o = o;
+  A.lse = lse;
+  A.Z = g.Z;
+  A.Y = g.Y;
+  A.X = g.X;
+  A.hq = g.Hq;
+  A.hkv = g.Hkv;
+  A.rz = g.rz;
+  A.ry = g.ry;
+  A.rx = g.rx;
+  A.c = g.scale * kLog2e;
+  A.tiles_y = (g.Y + C::TY - 1) / C::TY;
+  A.tiles_x = (g.X + C::TX - 1) / C::TX;
+  A.nblocks = (int64_t)A.tiles_x * A.tiles_y * g.Z * g.Hkv;
+  A.per_xcd = (A.nblocks + kNumXcd - 1) / kNumXcd;
+  hipLaunchKernelGGL(k_local_bf16<G>, dim3((unsigned)(A.per_xcd * kNumXcd)), dim3(64 * C::W), 0,
+                     s, A);
+  return hipGetLastError();
+}
+
+}  // namespace lb
+
+bool local_bf16_serves(int G) { return G == 4 || G == 8 || G == 16; }
+
+hipError_t launch_local_attn_bf16(const Geom& g, const void* q_rot, const void* k_rot,
+                                  const void* v, const int32_t* c2p, float* o_loc, float* lse,
+                                  hipStream_t s) {
+  switch (g.G) {
+    case 4: return lb::launch<4>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
+    case 8: return lb::launch<8>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
+    case 16: return lb::launch<16>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pack3d

@@ -158,8 +158,9 @@ const char* pack3d_last_error(void) { return g_err.c_str(); }
 const char* pack3d_backend_info(void) {
   return "libpack3d gfx950: rope=k_rope (VALU, 16B rows); "
          "block_summary=k_block_summary (wave per block, XOR-tree reduction); "
-         "local_attn=k_local_attn (LDS plane tiles + halo, masked-dense MFMA 32x32x16 bf16 / "
-         "32x32x2 f32); global_attn=k_global_attn (LDS double-buffered summary tiles, "
+         "local_attn=k_local_bf16 for bf16 with Hq/Hkv in {4,8,16} (async double-buffered "
+         "LDS planes, transposing V reads, masked-dense MFMA 32x32x16 bf16), else k_local_attn "
+         "(LDS plane tiles + halo, masked-dense MFMA 32x32x16 bf16 / 32x32x2 f32); global_attn=k_global_attn (LDS double-buffered summary tiles, "
          "MFMA 32x32x16 bf16 / 32x32x2 f32, online softmax, fused gate epilogue in forward); "
          "gate_mix=k_gate_mix; no fallbacks";
 }

@@ -50,6 +50,12 @@ hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, hipStream
 hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot,
                              const void* v, const int32_t* cell_to_pos, float* o_loc,
                              float* lse, hipStream_t s);
+// The bf16 kernel with compile-time plane geometry serves these group sizes;
+// launch_local_attn dispatches to it.
+bool local_bf16_serves(int G);
+hipError_t launch_local_attn_bf16(const Geom& g, const void* q_rot, const void* k_rot,
+                                  const void* v, const int32_t* cell_to_pos, float* o_loc,
+                                  float* lse, hipStream_t s);
 // o_cmp != nullptr: write o_cmp (fp32).  Otherwise gate-mix epilogue:
 // out = g_loc*o_loc + g_cmp*o_cmp in the problem dtype.  kmax != nullptr:
 // the key summaries are pre-scaled by scale*log2(e) and kmax[g] bounds their

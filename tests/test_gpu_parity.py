@@ -41,6 +41,10 @@ SMALL = [
     _w("g2_bf16_uniform", (5, 8, 16), 4, 2, "bf16", window=(5, 5, 5), weights="uniform",
        packing="block"),
     _w("tiny_lattice_f32", (1, 4, 4), 4, 2, "f32", window=(3, 7, 7)),
+    _w("g8_bf16", (3, 12, 12), 8, 1, "bf16"),
+    _w("g16_bf16_full", (3, 4, 12), 16, 1, "bf16", packing="morton"),
+    _w("g4_bf16_deep", (9, 12, 8), 8, 2, "bf16", window=(7, 3, 5), packing="morton"),
+    _w("g4_bf16_w1", (2, 8, 8), 4, 1, "bf16", window=(1, 1, 1), packing="raster"),
 ]
 IDS = [w.name for w in SMALL]
 
