@@ -185,19 +185,21 @@ def main() -> int:
     summary = work["summary_bytes"] + w.n_kv_heads * w.n_blocks * 4
     gbs = lambda b, t: b / (t * 1e-3) / 1e9
     tfl = lambda f, t: f / (t * 1e-3) / 1e12
+    # kernel serving each stage (see pack3d_backend_info)
+    local_kernel = ("k_local_bf16" if w.dtype == "bf16" and w.n_q_heads // w.n_kv_heads in (4, 8, 16)
+                    else "k_local_attn")
     kernels = {
-        "k_rope(q)": {"ms": stages["k_rope(q)"], "bound": "hbm",
-                      "gbs": gbs(rope_q, stages["k_rope(q)"])},
-        "k_rope(k_loc)": {"ms": stages["k_rope(k_loc)"], "bound": "hbm",
-                          "gbs": gbs(rope_k, stages["k_rope(k_loc)"])},
-        "k_block_summary": {"ms": stages["k_block_summary"], "bound": "hbm",
-                            "gbs": gbs(summary, stages["k_block_summary"])},
-        "k_kmax": {"ms": stages["k_kmax"], "bound": "launch"},
-        "k_local_attn": {"ms": stages["k_local_attn"], "bound": "mfma",
-                         "tflops": tfl(work["local_flops"], stages["k_local_attn"])},
-        "k_global_attn(gated)": {"ms": stages["k_global_attn(gated)"], "bound": "mfma",
-                                 "tflops": tfl(work["global_flops"],
-                                               stages["k_global_attn(gated)"])},
+        "k_rope(q)": {"ms": stages["rope(q)"], "bound": "hbm",
+                      "gbs": gbs(rope_q, stages["rope(q)"])},
+        "k_rope(k_loc)": {"ms": stages["rope(k_loc)"], "bound": "hbm",
+                          "gbs": gbs(rope_k, stages["rope(k_loc)"])},
+        "k_block_summary": {"ms": stages["block_summary"], "bound": "hbm",
+                            "gbs": gbs(summary, stages["block_summary"])},
+        "k_kmax": {"ms": stages["kmax"], "bound": "launch"},
+        local_kernel: {"ms": stages["local_attn"], "bound": "mfma",
+                       "tflops": tfl(work["local_flops"], stages["local_attn"])},
+        "k_global_attn(gated)": {"ms": stages["global_attn+gate"], "bound": "mfma",
+                                 "tflops": tfl(work["global_flops"], stages["global_attn+gate"])},
     }
     for v in kernels.values():
         if v["bound"] == "hbm":

@@ -33,11 +33,6 @@ namespace pack3d {
 constexpr int kGWaves = 8;
 constexpr int kGKt = 64;           // keys per LDS tile
 constexpr int kGVld = kGKt + 4;    // fp32 V^T row pitch (elements)
-constexpr float kRefHeadroom = 64.0f;   // fixed reference keeps exponentials <= 2^64
-constexpr float kSafeBound = 80.0f;     // ... for logit bounds up to this (log2 units)
-constexpr float kBoundMargin = 1.015625f;  // covers bf16 rounding of q, k~ and fp32 sums
-
-enum GMode : int { kGeneral = 0, kFixedRef = 1, kZeroRef = 2 };
 
 template <typename T> struct GCfg { static constexpr int kCb = 2; };   // column blocks / wave
 template <> struct GCfg<float> { static constexpr int kCb = 1; };
@@ -64,9 +59,9 @@ struct GArgs {
 
 // ---------------------------------------------------------------------------
 // LDS tiles.  bf16: K and V both row-major [64 keys][64 dims], chunk c of key
-// row r stored at chunk c ^ (r & 7) (K) or c ^ (2r & 6) (V: the transposing
-// read takes 4 consecutive keys x 16 dims per 16 lanes).  fp32: K as above,
-// V transposed [64 dims][kGVld].
+// row r stored at chunk c ^ ((r >> 1) & 7) (K, see KLds) or c ^ (2r & 6) (V:
+// the transposing read takes 4 consecutive keys x 16 dims per 16 lanes).
+// fp32: K as above, V transposed [64 dims][kGVld].
 // ---------------------------------------------------------------------------
 template <typename T>
 struct GLds {

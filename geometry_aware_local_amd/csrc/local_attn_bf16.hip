@@ -53,8 +53,7 @@ struct Cfg {
   static_assert(PY * PX * G == 32, "a patch is one MFMA column block");
   static_assert(W <= 16, "at most 1024 threads");
   static_assert(NKB * 4 >= KY, "key rows fit the key blocks");
-  // a key block is 4 region rows: keeps the K swizzle of a lane's row
-  static_assert((4 * RX) % 8 == 0, "block stride keeps the K swizzle");
+  static_assert(RX % 2 == 0, "a cell's bank half is the parity of its column");
 };
 
 struct Args {
@@ -72,10 +71,16 @@ struct Args {
   int64_t per_xcd;
 };
 
-// 16-byte chunk positions in a 128-byte LDS row: K spreads 8 consecutive
-// rows over all banks for the MFMA A operand; V spreads 4 consecutive rows
-// for the transposing reads.
-__device__ __forceinline__ int k_swz(int cell, int chunk) { return chunk ^ (cell & 7); }
+// 16-byte chunk positions in a cell's 128-byte LDS row.  gfx950 LDS has 64
+// four-byte banks and serves a 128-bit read 16 lanes at a time; a cell
+// (y, x) of the region sits in bank half x & 1 (RX is even).  A K operand
+// read takes 8 consecutive columns of 2 consecutive region rows per 16
+// lanes, so the position depends on (x >> 1) and on the row parity: all 16
+// (half, position) pairs differ.  V: the transposing read takes 4
+// consecutive cells x 16 dims per 16 lanes.
+__device__ __forceinline__ int k_swz(int y, int x, int chunk) {
+  return chunk ^ (((x >> 1) + 4 * (y & 1)) & 7);
+}
 __device__ __forceinline__ int v_swz(int cell, int chunk) { return chunk ^ ((2 * cell) & 6); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
       if (pc < RCP / 8) {
         const int cell = pc * 8 + (lane >> 3), cp = lane & 7;
         const int64_t row = (int64_t)pos[i] * rstride;
-        __builtin_amdgcn_global_load_lds((const void*)(kg + row + k_swz(cell, cp) * 8),
+        __builtin_amdgcn_global_load_lds((const void*)(kg + row + k_swz(cell / RX, cell % RX, cp) * 8),
                                          (lds_ptr)(kl + pc * 512), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(vg + row + v_swz(cell, cp) * 8),
                                          (lds_ptr)(vl + pc * 512), 16, 0, 0);
@@ -169,10 +174,11 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
   sm.l = 0.0f;
 
   // LDS element offsets of this lane's operand rows within a slot
-  const int kcell = (py0 + col / 8) * RX + px0 + col % 8;   // + 4*RX cells per key block
+  // + 4*RX cells per key block (4 rows: the row parity, hence the swizzle, stays)
+  const int ky0 = py0 + col / 8, kx0 = px0 + col % 8, kcell = ky0 * RX + kx0;
   int koff[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) koff[st] = kcell * 64 + k_swz(kcell, h * 4 + st) * 8;
+  for (int st = 0; st < 4; ++st) koff[st] = kcell * 64 + k_swz(ky0, kx0, h * 4 + st) * 8;
   const int r4 = lane & 15;
   int voff[2][2];   // [half][dim block]; + (4*kb + 2t)*RX cells per PV step
 #pragma unroll

@@ -209,8 +209,13 @@ __device__ __forceinline__ void load_qfrag(QFrag<T>& q, const T* row_h /* row + 
 // ---------------------------------------------------------------------------
 // LDS tile layouts.
 //
-// K rows: [rows][64] elements with the 16-byte chunks of row r XOR-swizzled
-// by (r & 7), so the 32 rows read by one MFMA operand spread over all banks.
+// K rows: [rows][64] elements with the 16-byte chunks of each row XOR-
+// swizzled so that the rows read by one MFMA operand spread over all banks.
+// gfx950 LDS has 64 four-byte banks (256 bytes) and serves a 128-bit read 16
+// lanes at a time: a bf16 row is 128 bytes, so rows r and r+1 sit in
+// different bank halves and the 8 rows of one parity among 16 consecutive
+// rows need distinct chunk positions (swizzle (r >> 1) & 7); an fp32 row is
+// 256 bytes and 16 consecutive rows need distinct positions (r & 15).
 // V^T: [64 dims][ld] elements, ld = key capacity + 4, so consecutive dims
 // start on different banks.
 // ---------------------------------------------------------------------------
@@ -219,7 +224,8 @@ struct KLds {
   static constexpr int kChunkElems = 16 / sizeof(T);       // elements per 16 B
   static constexpr int kChunks = 64 / kChunkElems;          // chunks per row
   __device__ static __forceinline__ int chunk_off(int row, int chunk) {
-    return row * 64 + ((chunk ^ (row & 7)) * kChunkElems);
+    const int sw = sizeof(T) == 2 ? (row >> 1) & 7 : row & 15;
+    return row * 64 + ((chunk ^ sw) * kChunkElems);
   }
 };
 
@@ -300,5 +306,16 @@ struct SoftmaxState {
 // 2^kRescaleSlack.  The decision is per column; skipping the O update when no
 // column moves changes no value (the factor would be exactly 1).
 constexpr float kRescaleSlack = 8.0f;
+
+// Softmax references of the query->summary kernels.  Given the largest
+// summary norm kmax of a group, every logit of query q lies within
+// +-|q| kmax (Cauchy-Schwarz); a column whose bound B (with a margin for the
+// bf16 rounding of q and k~ and the fp32 sums) is at most kSafeBound uses the
+// fixed reference max(0, B - kRefHeadroom), so its exponentials stay in
+// [2^-96, 2^64]; other columns track a lazily updated running max.
+constexpr float kRefHeadroom = 64.0f;
+constexpr float kSafeBound = 80.0f;
+constexpr float kBoundMargin = 1.015625f;
+enum GMode : int { kGeneral = 0, kFixedRef = 1, kZeroRef = 2 };
 
 }  // namespace pack3d
