@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the PACK3D local-global attention forward.
+"""fp64 CPU oracle of the PACK3D local-global attention forward and backward.
 
 TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously correct
 statement of what the operator computes.  Only ``tests/``, the smoke check in
@@ -36,6 +36,11 @@ single constant; the full list with reasons is kept with the design notes):
 * KV groups: query head h reads KV group h // (Hq / Hkv).
 * gate: one 2-way softmax per token (index 0 = local, 1 = compressed), or
   one per token and head when logits are [N, Hq, 2].
+* backward: the pages print no backward; the gradients below are the exact
+  derivatives of the forward above (chain rule through the gate, the two
+  softmax attentions, the block sums and the rotations) for an upstream
+  gradient of the output.  The weights ``a`` are treated as given (no
+  gradient is returned for them).
 """
 
 from __future__ import annotations
@@ -49,6 +54,8 @@ __all__ = [
     "axial_frequencies", "rotation_matrix", "rotate", "block_index",
     "block_summaries", "local_attention", "global_attention", "gate_weights",
     "gate_mix", "forward", "local_window_sizes",
+    "rotate_transpose", "local_attention_backward", "global_attention_backward",
+    "block_summaries_backward", "gate_backward", "backward",
 ]
 
 
@@ -315,3 +322,191 @@ def forward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits,
     out = gate_mix(o_loc, o_cmp, g)
     return dict(out=out, o_loc=o_loc, o_cmp=o_cmp, lse_loc=lse_loc, lse_cmp=lse_cmp,
                 k_sum=k_sum, v_sum=v_sum, q_rot=q_rot, k_rot=k_rot)
+
+
+# ----------------------------------------------------------------------------
+# Backward.  The operator is a block of a trained network (papernotes.org
+# notes, the loss / training paragraph); its gradients are the derivatives of
+# the forward above.  For one softmax attention o = sum_u p_u v_u with
+# p = softmax(scale * <q, k_u>) and upstream gradient g:
+#   dp_u = <g, v_u>,  D = sum_u p_u dp_u (= <g, o>),  ds_u = p_u (dp_u - D),
+#   dq = scale * sum_u ds_u k_u,  dk_u = scale * ds_u q,  dv_u = p_u g.
+# ----------------------------------------------------------------------------
+
+def rotate_transpose(x: np.ndarray, coords: np.ndarray,
+                     rope_pairs: Sequence[int] = (11, 11, 10),
+                     base: float = 10000.0) -> np.ndarray:
+    """R(c_i)^T x_{i,h}: each 2x2 block of R(c) transposed (the inverse)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = x.copy()
+    omega = axial_frequencies(rope_pairs, base)
+    p = 0
+    for a, m in enumerate(rope_pairs):
+        ca = np.asarray(coords[:, a], dtype=np.float64)
+        for r in range(m):
+            th = omega[a][r] * ca
+            cs, sn = np.cos(th)[:, None], np.sin(th)[:, None]
+            x0, x1 = x[:, :, 2 * p], x[:, :, 2 * p + 1]
+            y[:, :, 2 * p] = cs * x0 + sn * x1
+            y[:, :, 2 * p + 1] = -sn * x0 + cs * x1
+            p += 1
+    return y
+
+
+def local_attention_backward(q_rot: np.ndarray, k_rot: np.ndarray, v: np.ndarray,
+                             coords: np.ndarray, grid: Sequence[int], window: Sequence[int],
+                             scale: float, d_out: np.ndarray,
+                             rows: Optional[np.ndarray] = None, chunk: int = 4096):
+    """Gradients of the local branch for upstream ``d_out`` [N, Hq, D].
+
+    Returns ``(dq [R, Hq, D], dk [N, Hkv, D], dv [N, Hkv, D])``: ``dq`` for the
+    query rows ``rows`` (default all) and the contributions of those rows to
+    every key.  The window is symmetric (u in N(i) iff i in N(u)), so ``dk``
+    and ``dv`` are exact at every key whose own window lies inside ``rows``.
+    """
+    grid = tuple(int(g) for g in grid)
+    n = k_rot.shape[0]
+    hq, d = q_rot.shape[1:]
+    hkv = k_rot.shape[1]
+    grp = hq // hkv
+    coords = np.asarray(coords, np.int64)
+    lattice = np.full(grid, -1, dtype=np.int64)
+    lattice[coords[:, 0], coords[:, 1], coords[:, 2]] = np.arange(n)
+    offs = np.array(_window_offsets(window), dtype=np.int64)
+    rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
+    gmax = np.array(grid, dtype=np.int64) - 1
+    dq = np.zeros((len(rows), hq, d))
+    dk = np.zeros((n, hkv, d))
+    dv = np.zeros((n, hkv, d))
+    for s in range(0, len(rows), chunk):
+        r = rows[s:s + chunk]
+        nr = len(r)
+        qc = np.asarray(q_rot[r], np.float64).reshape(nr, hkv, grp, d)
+        gc = np.asarray(d_out[r], np.float64).reshape(nr, hkv, grp, d)
+        ci = coords[r]
+        pos = np.zeros((nr, len(offs)), dtype=np.int64)
+        valid = np.zeros((nr, len(offs)), dtype=bool)
+        logit = np.full((nr, len(offs), hkv, grp), -np.inf)
+        dp = np.zeros((nr, len(offs), hkv, grp))
+        for t, off in enumerate(offs):
+            cu = ci + off
+            ok = np.all((cu >= 0) & (cu <= gmax), axis=1)
+            cc = np.clip(cu, 0, gmax)
+            pu = lattice[cc[:, 0], cc[:, 1], cc[:, 2]]
+            ku = np.asarray(k_rot[pu], np.float64)
+            vu = np.asarray(v[pu], np.float64)
+            logit[:, t] = np.where(ok[:, None, None], scale * np.einsum("nkgd,nkd->nkg", qc, ku),
+                                   -np.inf)
+            dp[:, t] = np.einsum("nkgd,nkd->nkg", gc, vu)
+            pos[:, t], valid[:, t] = pu, ok
+        mx = logit.max(axis=1, keepdims=True)
+        e = np.exp(logit - mx)
+        p = e / e.sum(axis=1, keepdims=True)                      # [nr, T, hkv, grp]
+        big_d = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * (dp - big_d)
+        dqc = np.zeros((nr, hkv, grp, d))
+        for t in range(len(offs)):
+            ok = valid[:, t]
+            pu = pos[ok, t]
+            ku = np.asarray(k_rot[pu], np.float64)
+            dqc[ok] += scale * ds[ok, t][..., None] * ku[:, :, None, :]
+            np.add.at(dk, pu, scale * np.einsum("nkg,nkgd->nkd", ds[ok, t], qc[ok]))
+            np.add.at(dv, pu, np.einsum("nkg,nkgd->nkd", p[ok, t], gc[ok]))
+        dq[s:s + nr] = dqc.reshape(nr, hq, d)
+    return dq, dk, dv
+
+
+def global_attention_backward(q_rot: np.ndarray, k_sum: np.ndarray, v_sum: np.ndarray,
+                              scale: float, d_out: np.ndarray,
+                              rows: Optional[np.ndarray] = None):
+    """Gradients of the query->summary branch for upstream ``d_out``.
+
+    Returns ``(dq [R, Hq, D], dk_sum [Hkv, M, D], dv_sum [Hkv, M, D])`` for the
+    query rows ``rows`` (default all); the summary gradients hold the
+    contributions of those rows.
+    """
+    n, hq, d = q_rot.shape
+    hkv, m, _ = k_sum.shape
+    grp = hq // hkv
+    rows = np.arange(n) if rows is None else np.asarray(rows, np.int64)
+    dq = np.zeros((len(rows), hq, d))
+    dk = np.zeros((hkv, m, d))
+    dv = np.zeros((hkv, m, d))
+    chunk = max(1, (1 << 23) // (grp * m))
+    for s in range(0, len(rows), chunk):
+        r = rows[s:s + chunk]
+        for g in range(hkv):
+            kg = np.asarray(k_sum[g], np.float64)
+            vg = np.asarray(v_sum[g], np.float64)
+            qg = np.asarray(q_rot[r, g * grp:(g + 1) * grp], np.float64).reshape(-1, d)
+            gg = np.asarray(d_out[r, g * grp:(g + 1) * grp], np.float64).reshape(-1, d)
+            t = scale * (qg @ kg.T)
+            e = np.exp(t - t.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)                  # [R*grp, M]
+            dp = gg @ vg.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[s:s + len(r), g * grp:(g + 1) * grp] = (scale * (ds @ kg)).reshape(len(r), grp, d)
+            dk[g] += scale * (ds.T @ qg)
+            dv[g] += p.T @ gg
+    return dq, dk, dv
+
+
+def block_summaries_backward(dk_sum: np.ndarray, dv_sum: np.ndarray, a: Optional[np.ndarray],
+                             coords: np.ndarray, grid: Sequence[int], block: Sequence[int],
+                             rope_pairs: Sequence[int] = (11, 11, 10), base: float = 10000.0):
+    """Gradients of (k~, v~) with respect to (k_cmp, v_cmp): since
+    k~_j = sum_{u in B_j} a_u R(c_u) k_u and v~_j = sum a_u v_u,
+    dk_u = a_u R(c_u)^T dk~_j(u) and dv_u = a_u dv~_j(u)."""
+    hkv, m, d = dk_sum.shape
+    n = len(coords)
+    vol = int(np.prod(block))
+    w = (np.full((n, hkv), 1.0 / vol) if a is None else np.asarray(a, dtype=np.float64))
+    j = block_index(coords, grid, block)
+    gk = np.asarray(dk_sum, np.float64)[:, j].transpose(1, 0, 2)      # [N, Hkv, D]
+    gv = np.asarray(dv_sum, np.float64)[:, j].transpose(1, 0, 2)
+    dk = rotate_transpose(w[:, :, None] * gk, coords, rope_pairs, base)
+    dv = w[:, :, None] * gv
+    return dk, dv
+
+
+def gate_backward(gate_logits: np.ndarray, d_out: np.ndarray, o_loc: np.ndarray,
+                  o_cmp: np.ndarray):
+    """Gradients through O = g_loc o_loc + g_cmp o_cmp, g = softmax(logits).
+
+    Returns ``(dgate, d_loc, d_cmp)``: the logits' gradient (same shape as
+    the logits) and the upstream gradients of the two branches, g_b * d_out.
+    With one gate per token the gate's gradient sums over heads.
+    """
+    g = gate_weights(gate_logits)
+    gh = g[:, None, :] if g.ndim == 2 else g
+    d_out = np.asarray(d_out, np.float64)
+    dg_loc = (d_out * o_loc).sum(axis=-1)                              # [N, Hq]
+    dg_cmp = (d_out * o_cmp).sum(axis=-1)
+    if g.ndim == 2:
+        dg_loc, dg_cmp = dg_loc.sum(axis=1), dg_cmp.sum(axis=1)
+    # softmax Jacobian of two logits: dl0 = g0 g1 (dg0 - dg1) = -dl1
+    t = g[..., 0] * g[..., 1] * (dg_loc - dg_cmp)
+    dgate = np.stack([t, -t], axis=-1)
+    return dgate, gh[..., 0:1] * d_out, gh[..., 1:2] * d_out
+
+
+def backward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits, d_out,
+             scale: Optional[float] = None) -> dict:
+    """All input gradients of the forward for the upstream gradient ``d_out``
+    of its output: dq, dk_loc, dv_loc, dk_cmp, dv_cmp and dgate (plus the
+    branch intermediates).  ``p`` as in :func:`forward`."""
+    tau = 1.0 / math.sqrt(p.head_dim) if scale is None else scale
+    coords = np.asarray(coords)
+    f = forward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits, scale=tau)
+    dgate, d_loc, d_cmp = gate_backward(gate_logits, d_out, f["o_loc"], f["o_cmp"])
+    dq_l, dk_r, dv_loc = local_attention_backward(f["q_rot"], f["k_rot"], v_loc, coords, p.grid,
+                                                  p.window, tau, d_loc)
+    dq_c, dk_sum, dv_sum = global_attention_backward(f["q_rot"], f["k_sum"], f["v_sum"], tau,
+                                                     d_cmp)
+    dq = rotate_transpose(dq_l + dq_c, coords, p.rope_pairs, p.rope_base)
+    dk_loc = rotate_transpose(dk_r, coords, p.rope_pairs, p.rope_base)
+    dk_cmp, dv_cmp = block_summaries_backward(dk_sum, dv_sum, a, coords, p.grid, p.block,
+                                              p.rope_pairs, p.rope_base)
+    return dict(dq=dq, dk_loc=dk_loc, dv_loc=dv_loc, dk_cmp=dk_cmp, dv_cmp=dv_cmp,
+                dgate=dgate, dk_sum=dk_sum, dv_sum=dv_sum, d_loc=d_loc, d_cmp=d_cmp,
+                fwd=f)

@@ -227,3 +227,17 @@ def make_inputs(w: Workload, explicit_uniform: bool = False) -> Inputs:
     take = lambda t: None if t is None else np.ascontiguousarray(t[order])
     return Inputs(w, order, coords, c2p, take(q), take(k_loc), take(v_loc), take(k_cmp),
                   take(v_cmp), take(a), take(gate))
+
+
+def make_upstream_grad(inp: Inputs, seed_offset: int = 200) -> np.ndarray:
+    """Upstream gradient of the output, ``[N, Hq, D]`` ~ N(0, 1), drawn per
+    lattice cell in raster order from ``default_rng(seed + seed_offset)`` and
+    then placed in the inputs' packing (bf16-rounded for bf16 workloads), so
+    every packing of a workload carries the same per-cell gradient."""
+    w = inp.workload
+    rng = np.random.default_rng(w.seed + seed_offset)
+    g = rng.standard_normal((w.n_tokens, w.n_q_heads, w.head_dim), dtype=np.float32)
+    if w.dtype == "bf16":
+        g = round_to_bf16(g)
+    # inp.order[i] is the raster cell at packed position i
+    return np.ascontiguousarray(g[inp.order])
