@@ -21,40 +21,11 @@
 // window or outside the lattice are masked to -inf and an online softmax
 // carries the state across planes.  Every reduction order is fixed by
 // coordinates, never by packing.
-#include "pack3d_device.h"
+#include "local_tiles.h"
 
 namespace pack3d {
 
 namespace lb {
-
-constexpr int kHalo = 3;     // largest supported y/x radius
-constexpr int kKx = 8;       // key slots per row: patch width 2 + 2 * halo
-
-template <int G> struct Shape;   // patch PY x 2 cells, tile TY x TX cells
-template <> struct Shape<4> { static constexpr int PY = 4, TY = 8, TX = 8; };
-template <> struct Shape<8> { static constexpr int PY = 2, TY = 8, TX = 4; };
-template <> struct Shape<16> { static constexpr int PY = 1, TY = 4, TX = 4; };
-
-template <int G>
-struct Cfg {
-  static constexpr int PY = Shape<G>::PY, PX = 2, TY = Shape<G>::TY, TX = Shape<G>::TX;
-  static constexpr int KY = PY + 2 * kHalo;                 // key rows per plane
-  static constexpr int NKB = (KY * kKx + 31) / 32;          // 32-key blocks per plane
-  static constexpr int RX = TX - PX + kKx;                  // region width (cells)
-  static constexpr int RY = TY + 2 * kHalo;
-  static constexpr int RC = RX * RY;                        // region cells
-  static constexpr int RCP = (RC + 7) / 8 * 8;              // padded to 1 KB pieces
-  // key blocks round a patch's key rows up to 4*NKB: the last patch row
-  // reaches region row TY - PY + 4*NKB - 1, so the slot holds that many rows
-  // (the rows past RY are zero, never copied, and always masked)
-  static constexpr int RYA = TY - PY + 4 * NKB > RY ? TY - PY + 4 * NKB : RY;
-  static constexpr int RCA = RYA * RX > RCP ? RYA * RX : RCP;   // cells per slot
-  static constexpr int W = TY * TX / (PY * PX);             // waves = patches
-  static_assert(PY * PX * G == 32, "a patch is one MFMA column block");
-  static_assert(W <= 16, "at most 1024 threads");
-  static_assert(NKB * 4 >= KY, "key rows fit the key blocks");
-  static_assert(RX % 2 == 0, "a cell's bank half is the parity of its column");
-};
 
 struct Args {
   const bf16_t* q;
@@ -70,20 +41,6 @@ struct Args {
   int64_t nblocks;
   int64_t per_xcd;
 };
-
-// 16-byte chunk positions in a cell's 128-byte LDS row.  gfx950 LDS has 64
-// four-byte banks and serves a 128-bit read 16 lanes at a time; a cell
-// (y, x) of the region sits in bank half x & 1 (RX is even).  A K operand
-// read takes 8 consecutive columns of 2 consecutive region rows per 16
-// lanes, so the position depends on (x >> 1) and on the row parity: all 16
-// (half, position) pairs differ.  V: the transposing read takes 4
-// consecutive cells x 16 dims per 16 lanes.
-__device__ __forceinline__ int k_swz(int y, int x, int chunk) {
-  return chunk ^ (((x >> 1) + 4 * (y & 1)) & 7);
-}
-__device__ __forceinline__ int v_swz(int cell, int chunk) { return chunk ^ ((2 * cell) & 6); }
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 template <int G>
 __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {

@@ -147,6 +147,62 @@ WsLayout ws_layout(const Geom& g) {
   return w;
 }
 
+// The forward's saved state for the backward: o_loc, o_cmp fp32 [N, Hq, 64],
+// lse_loc, lse_cmp fp32 [N, Hq].
+struct SavedLayout {
+  size_t o_loc, o_cmp, lse_loc, lse_cmp, total;
+};
+
+SavedLayout saved_layout(const Geom& g) {
+  SavedLayout l;
+  size_t off = 0;
+  l.o_loc = off;
+  off += align256((size_t)g.N * g.Hq * 64 * 4);
+  l.o_cmp = off;
+  off += align256((size_t)g.N * g.Hq * 64 * 4);
+  l.lse_loc = off;
+  off += align256((size_t)g.N * g.Hq * 4);
+  l.lse_cmp = off;
+  off += align256((size_t)g.N * g.Hq * 4);
+  l.total = off;
+  return l;
+}
+
+struct BwdLayout {
+  size_t q_rot, k_rot, k_sum, v_sum, dlo, dco, d_loc, d_cmp, dq_acc, dk_part, dv_part, total;
+};
+
+BwdLayout bwd_layout(const Geom& g) {
+  BwdLayout w;
+  const size_t nsplit = (size_t)glob_dkv_splits(g);
+  size_t off = 0;
+  auto take = [&](size_t& at, size_t bytes) {
+    at = off;
+    off += align256(bytes);
+  };
+  take(w.q_rot, (size_t)g.N * g.Hq * 64 * 2);
+  take(w.k_rot, (size_t)g.N * g.Hkv * 64 * 2);
+  take(w.k_sum, (size_t)g.Hkv * g.M * 64 * 2);
+  take(w.v_sum, (size_t)g.Hkv * g.M * 64 * 2);
+  take(w.dlo, (size_t)g.N * g.Hq * 64 * 2);
+  take(w.dco, (size_t)g.N * g.Hq * 64 * 2);
+  take(w.d_loc, (size_t)g.N * g.Hq * 4);
+  take(w.d_cmp, (size_t)g.N * g.Hq * 4);
+  take(w.dq_acc, (size_t)g.N * g.Hq * 64 * 4);
+  take(w.dk_part, nsplit * g.Hkv * g.M * 64 * 4);
+  take(w.dv_part, nsplit * g.Hkv * g.M * 64 * 4);
+  w.total = off;
+  return w;
+}
+
+int check_buffer(void* p, size_t have, size_t need, const char* fn, const char* what) {
+  if (!p) return fail(PACK3D_ERR_WORKSPACE, "%s: %s is NULL", fn, what);
+  if (have < need)
+    return fail(PACK3D_ERR_WORKSPACE, "%s: %s %zu bytes < %zu needed", fn, what, have, need);
+  if ((uintptr_t)p & 255) return fail(PACK3D_ERR_WORKSPACE, "%s: %s not 256-byte aligned", fn, what);
+  return PACK3D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,7 +218,9 @@ const char* pack3d_backend_info(void) {
          "LDS planes, transposing V reads, masked-dense MFMA 32x32x16 bf16), else k_local_attn "
          "(LDS plane tiles + halo, masked-dense MFMA 32x32x16 bf16 / 32x32x2 f32); global_attn=k_global_attn (LDS double-buffered summary tiles, "
          "MFMA 32x32x16 bf16 / 32x32x2 f32, online softmax, fused gate epilogue in forward); "
-         "gate_mix=k_gate_mix; no fallbacks";
+         "gate_mix=k_gate_mix; backward (bf16, Hq/Hkv in {4,8,16}): k_bwd_prep, k_loc_dq, "
+         "k_glob_dq, k_unrotate, k_loc_dkv, k_glob_dkv, k_sum_bwd (MFMA 32x32x16 bf16); "
+         "no fallbacks";
 }
 
 size_t pack3d_forward_workspace_size(const pack3d_problem* prob) {
@@ -346,6 +404,133 @@ int pack3d_check_packing(const pack3d_problem* prob, const int32_t* coords,
     return fail(PACK3D_ERR_NULL, "pack3d_check_packing: NULL tensor argument");
   return hip_status(launch_check_packing(g, coords, cell_to_pos, n_bad_dev, (hipStream_t)stream),
                     "k_check_packing");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t pack3d_saved_size(const pack3d_problem* prob) {
+  Geom g;
+  if (make_geom(prob, &g) != PACK3D_OK) return 0;
+  return saved_layout(g).total;
+}
+
+size_t pack3d_backward_workspace_size(const pack3d_problem* prob) {
+  Geom g;
+  if (make_geom(prob, &g) != PACK3D_OK) return 0;
+  return bwd_layout(g).total;
+}
+
+int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* k_loc,
+                         const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                         const int32_t* coords, const int32_t* cell_to_pos,
+                         const float* gate_logits, void* out, void* saved, size_t saved_bytes,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  static const char* fn = "pack3d_forward_train";
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!q || !k_loc || !v_loc || !k_cmp || !v_cmp || !coords || !cell_to_pos || !gate_logits ||
+      !out)
+    return fail(PACK3D_ERR_NULL, "%s: NULL tensor argument", fn);
+  if (!local_supported(g))
+    return fail(PACK3D_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d unsupported", fn, g.G);
+  const WsLayout w = ws_layout(g);
+  const SavedLayout sl = saved_layout(g);
+  if ((rc = check_buffer(workspace, ws_bytes, w.total, fn, "workspace"))) return rc;
+  if ((rc = check_buffer(saved, saved_bytes, sl.total, fn, "saved"))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  char* sv = (char*)saved;
+  void* q_rot = ws + w.q_rot;
+  void* k_rot = ws + w.k_rot;
+  void* k_sum = ws + w.k_sum;
+  void* v_sum = ws + w.v_sum;
+  float* knorm = (float*)(ws + w.knorm);
+  float* kmax = (float*)(ws + w.kmax);
+  float* o_loc = (float*)(sv + sl.o_loc);
+  float* o_cmp = (float*)(sv + sl.o_cmp);
+  float* lse_loc = (float*)(sv + sl.lse_loc);
+  float* lse_cmp = (float*)(sv + sl.lse_cmp);
+  hipError_t e;
+  if ((e = launch_rope(g, q, q_rot, g.Hq, coords, s)) != hipSuccess) return hip_status(e, "k_rope(q)");
+  if ((e = launch_rope(g, k_loc, k_rot, g.Hkv, coords, s)) != hipSuccess)
+    return hip_status(e, "k_rope(k_loc)");
+  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
+                                g.scale * 1.4426950408889634f, knorm, s)) != hipSuccess)
+    return hip_status(e, "k_block_summary");
+  if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
+  if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, lse_loc, s)) != hipSuccess)
+    return hip_status(e, "k_local_attn");
+  e = launch_global_attn(g, q_rot, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, nullptr, nullptr,
+                         nullptr, s);
+  if (e != hipSuccess) return hip_status(e, "k_global_attn");
+  return hip_status(launch_gate_mix(g, o_loc, o_cmp, gate_logits, out, s), "k_gate_mix");
+}
+
+int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc,
+                    const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                    const int32_t* coords, const int32_t* cell_to_pos, const float* gate_logits,
+                    const void* saved, size_t saved_bytes, const void* dout, void* dq,
+                    void* dk_loc, void* dv_loc, void* dk_cmp, void* dv_cmp, float* dgate,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  static const char* fn = "pack3d_backward";
+  Geom g;
+  int rc = make_geom(prob, &g);
+  if (rc) return rc;
+  if (!q || !k_loc || !v_loc || !k_cmp || !v_cmp || !coords || !cell_to_pos || !gate_logits ||
+      !dout || !dq || !dk_loc || !dv_loc || !dk_cmp || !dv_cmp || !dgate)
+    return fail(PACK3D_ERR_NULL, "%s: NULL tensor argument", fn);
+  if (!backward_supported(g))
+    return fail(PACK3D_ERR_UNSUPPORTED,
+                "%s: only bf16 with Hq/Hkv in {4, 8, 16} is supported (dtype %d, Hq/Hkv %d)", fn,
+                prob->dtype, g.G);
+  const BwdLayout w = bwd_layout(g);
+  const SavedLayout sl = saved_layout(g);
+  if ((rc = check_buffer(workspace, ws_bytes, w.total, fn, "workspace"))) return rc;
+  if ((rc = check_buffer((void*)saved, saved_bytes, sl.total, fn, "saved"))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const char* sv = (const char*)saved;
+  BwdBuffers b;
+  b.v_loc = v_loc;
+  b.a = a;
+  b.coords = coords;
+  b.c2p = cell_to_pos;
+  b.gate = gate_logits;
+  b.dout = dout;
+  b.o_loc = (const float*)(sv + sl.o_loc);
+  b.o_cmp = (const float*)(sv + sl.o_cmp);
+  b.lse_loc = (const float*)(sv + sl.lse_loc);
+  b.lse_cmp = (const float*)(sv + sl.lse_cmp);
+  b.q_rot = ws + w.q_rot;
+  b.k_rot = ws + w.k_rot;
+  b.k_sum = ws + w.k_sum;
+  b.v_sum = ws + w.v_sum;
+  b.dlo = ws + w.dlo;
+  b.dco = ws + w.dco;
+  b.d_loc = (float*)(ws + w.d_loc);
+  b.d_cmp = (float*)(ws + w.d_cmp);
+  b.dq_acc = (float*)(ws + w.dq_acc);
+  b.dk_part = (float*)(ws + w.dk_part);
+  b.dv_part = (float*)(ws + w.dv_part);
+  b.dq = dq;
+  b.dk_loc = dk_loc;
+  b.dv_loc = dv_loc;
+  b.dk_cmp = dk_cmp;
+  b.dv_cmp = dv_cmp;
+  b.dgate = dgate;
+  hipError_t e;
+  // recompute the rotations and the (unscaled) summaries
+  if ((e = launch_rope(g, q, ws + w.q_rot, g.Hq, coords, s)) != hipSuccess)
+    return hip_status(e, "k_rope(q)");
+  if ((e = launch_rope(g, k_loc, ws + w.k_rot, g.Hkv, coords, s)) != hipSuccess)
+    return hip_status(e, "k_rope(k_loc)");
+  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, ws + w.k_sum, ws + w.v_sum, 1.0f,
+                                nullptr, s)) != hipSuccess)
+    return hip_status(e, "k_block_summary");
+  return hip_status(launch_backward(g, b, s), fn);
 }
 
 }  // extern "C"

@@ -64,6 +64,40 @@ hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_su
                               const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
                               float* lse, const float* o_loc, const float* gate, void* out,
                               hipStream_t s);
+// Backward (bf16).  Inputs, the forward's saved state, workspace buffers and
+// outputs of one backward launch sequence.
+struct BwdBuffers {
+  const void* v_loc;           // [N, Hkv, 64]
+  const float* a;              // [N, Hkv] or NULL (uniform)
+  const int32_t* coords;       // [N, 3]
+  const int32_t* c2p;          // [Z*Y*X]
+  const float* gate;           // [N, 2] or [N, Hq, 2]
+  const void* dout;            // [N, Hq, 64]
+  const float* o_loc;          // saved [N, Hq, 64]
+  const float* o_cmp;          // saved [N, Hq, 64]
+  const float* lse_loc;        // saved [N, Hq]
+  const float* lse_cmp;        // saved [N, Hq]
+  const void* q_rot;           // workspace: rotated q, k_loc, unscaled summaries
+  const void* k_rot;
+  const void* k_sum;
+  const void* v_sum;
+  void* dlo;                   // workspace: g_loc * dO, g_cmp * dO (bf16)
+  void* dco;
+  float* d_loc;                // workspace: D of each branch [N, Hq]
+  float* d_cmp;
+  float* dq_acc;               // workspace: rotated-frame dq [N, Hq, 64]
+  float* dk_part;              // workspace: summary gradient partials
+  float* dv_part;              //   [splits, Hkv, M, 64]
+  void* dq;                    // outputs
+  void* dk_loc;
+  void* dv_loc;
+  void* dk_cmp;
+  void* dv_cmp;
+  float* dgate;
+};
+bool backward_supported(const Geom& g);
+int64_t glob_dkv_splits(const Geom& g);
+hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s);
 hipError_t launch_gate_mix(const Geom& g, const float* o_loc, const float* o_cmp,
                            const float* gate, void* out, hipStream_t s);
 hipError_t launch_build_cell_index(const Geom& g, const int32_t* coords, int32_t* c2p,

@@ -38,7 +38,8 @@ EXPORTS = (
     "pack3d_rope", "pack3d_block_summary", "pack3d_local_attn", "pack3d_global_attn",
     "pack3d_gate_mix", "pack3d_forward", "pack3d_forward_timed", "pack3d_forward_workspace_size",
     "pack3d_build_cell_index", "pack3d_check_packing", "pack3d_last_error",
-    "pack3d_backend_info", "pack3d_version",
+    "pack3d_backend_info", "pack3d_version", "pack3d_saved_size", "pack3d_forward_train",
+    "pack3d_backward_workspace_size", "pack3d_backward",
 )
 
 
@@ -94,12 +95,15 @@ def _load() -> ctypes.CDLL:
                                  ctypes.POINTER(ctypes.c_void_p), I32],
         "pack3d_build_cell_index": [P, V, V, V],
         "pack3d_check_packing": [P, V, V, V, V],
+        "pack3d_forward_train": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V, SZ, V],
+        "pack3d_backward": [P, V, V, V, V, V, V, V, V, V, V, SZ, V, V, V, V, V, V, V, V, SZ, V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes, fn.restype = args, ctypes.c_int
-    lib.pack3d_forward_workspace_size.argtypes = [P]
-    lib.pack3d_forward_workspace_size.restype = ctypes.c_size_t
+    for name in ("pack3d_forward_workspace_size", "pack3d_saved_size",
+                 "pack3d_backward_workspace_size"):
+        getattr(lib, name).argtypes, getattr(lib, name).restype = [P], ctypes.c_size_t
     for name in ("pack3d_last_error", "pack3d_backend_info"):
         getattr(lib, name).argtypes, getattr(lib, name).restype = [], ctypes.c_char_p
     lib.pack3d_version.argtypes, lib.pack3d_version.restype = [], ctypes.c_int
@@ -267,16 +271,18 @@ def _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, g
             _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
             _ptr(gate, torch.float32, gshape, "gate"), _ptr(out, dt, (n, hq, 64), "out"),
             ws.data_ptr(), ws.numel(), _stream(q.device))
-    return args, out
+    # the caller keeps ws alive until the launch: args hold only its address
+    return args, out, ws
 
 
 def pack3d_forward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
                    workspace: Optional[torch.Tensor] = None,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole forward: out [N, Hq, 64] in the input dtype."""
-    args, out = _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
-                              workspace, out)
+    args, out, ws = _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos,
+                                  gate, workspace, out)
     _check(LIB.pack3d_forward(*args))
+    del ws
     return out
 
 
@@ -292,10 +298,83 @@ def pack3d_forward_timed(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords
         if not e.cuda_event:
             e.record()
     handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
-    args, out = _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
-                              workspace, out)
+    args, out, ws = _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos,
+                                  gate, workspace, out)
     _check(LIB.pack3d_forward_timed(*args, handles, len(events)))
+    del ws
     return out
+
+
+def pack3d_saved_size(prob: Problem) -> int:
+    return int(LIB.pack3d_saved_size(ctypes.byref(prob)))
+
+
+def pack3d_backward_workspace_size(prob: Problem) -> int:
+    return int(LIB.pack3d_backward_workspace_size(ctypes.byref(prob)))
+
+
+def _buffer(size_fn, prob: Problem, device) -> torch.Tensor:
+    size = size_fn(prob)
+    if size == 0:
+        _check(-2)
+    return torch.empty(size, dtype=torch.uint8, device=device)
+
+
+def pack3d_forward_train(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos,
+                         gate, workspace: Optional[torch.Tensor] = None,
+                         saved: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None):
+    """The forward for training: returns ``(out, saved)``, ``saved`` holding
+    the state pack3d_backward needs (o_loc, o_cmp, lse_loc, lse_cmp)."""
+    args, out, ws = _forward_args(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos,
+                                  gate, workspace, out)
+    saved = _buffer(pack3d_saved_size, prob, q.device) if saved is None else saved
+    # C order: ..., out, saved, saved_bytes, workspace, ws_bytes, stream
+    _check(LIB.pack3d_forward_train(*args[:11], saved.data_ptr(), saved.numel(), *args[11:]))
+    del ws
+    return out, saved
+
+
+def saved_views(prob: Problem, saved: torch.Tensor) -> dict:
+    """fp32 views of the saved state: o_loc, o_cmp [N, Hq, 64], lse_loc,
+    lse_cmp [N, Hq] (each section 256-byte aligned)."""
+    n, hq = prob.n_tokens, prob.n_q_heads
+    a256 = lambda b: (b + 255) // 256 * 256
+    sizes = [("o_loc", n * hq * 64), ("o_cmp", n * hq * 64), ("lse_loc", n * hq),
+             ("lse_cmp", n * hq)]
+    out, off = {}, 0
+    for name, cnt in sizes:
+        t = saved[off:off + cnt * 4].view(torch.float32)
+        out[name] = t.view(n, hq, 64) if name.startswith("o_") else t.view(n, hq)
+        off += a256(cnt * 4)
+    return out
+
+
+def pack3d_backward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
+                    saved: torch.Tensor, dout: torch.Tensor,
+                    workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of the forward's output for upstream ``dout``: a dict with
+    dq [N,Hq,64], dk_loc, dv_loc, dk_cmp, dv_cmp [N,Hkv,64] (input dtype) and
+    dgate (fp32, the gate logits' shape)."""
+    n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
+    gshape = (n, hq, 2) if prob.gate_per_head else (n, 2)
+    ws = _buffer(pack3d_backward_workspace_size, prob, q.device) if workspace is None else workspace
+    g = {"dq": _empty((n, hq, 64), dt, q)}
+    for name in ("dk_loc", "dv_loc", "dk_cmp", "dv_cmp"):
+        g[name] = _empty((n, hkv, 64), dt, q)
+    g["dgate"] = _empty(gshape, torch.float32, q)
+    _check(LIB.pack3d_backward(
+        ctypes.byref(prob), _ptr(q, dt, (n, hq, 64), "q"),
+        _ptr(k_loc, dt, (n, hkv, 64), "k_loc"), _ptr(v_loc, dt, (n, hkv, 64), "v_loc"),
+        _ptr(k_cmp, dt, (n, hkv, 64), "k_cmp"), _ptr(v_cmp, dt, (n, hkv, 64), "v_cmp"),
+        _ptr(a, torch.float32, (n, hkv), "a"), _ptr(coords, torch.int32, (n, 3), "coords"),
+        _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
+        _ptr(gate, torch.float32, gshape, "gate"), _ptr(saved, torch.uint8, None, "saved"),
+        saved.numel(), _ptr(dout, dt, (n, hq, 64), "dout"), g["dq"].data_ptr(),
+        g["dk_loc"].data_ptr(), g["dv_loc"].data_ptr(), g["dk_cmp"].data_ptr(),
+        g["dv_cmp"].data_ptr(), g["dgate"].data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream(q.device)))
+    return g
 
 
 def pack3d_build_cell_index(prob: Problem, coords: torch.Tensor) -> torch.Tensor:

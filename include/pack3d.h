@@ -189,6 +189,51 @@ int pack3d_forward_timed(const pack3d_problem* prob, const void* q, const void* 
                          const float* gate_logits, void* out, void* workspace, size_t ws_bytes,
                          void* stream, void* const* events, int32_t n_events);
 
+/*
+ * Training forward: the same output as pack3d_forward, plus, in `saved`, the
+ * state pack3d_backward needs: o_loc fp32 [N, Hq, 64], o_cmp fp32
+ * [N, Hq, 64], lse_loc fp32 [N, Hq], lse_cmp fp32 [N, Hq] (natural-log
+ * log-sum-exp of each branch's scaled logits), in that order, each section
+ * starting on a 256-byte boundary.  saved: device memory of at least
+ * pack3d_saved_size() bytes, 256-byte aligned, caller-owned.  The gate is
+ * applied by a separate pass over the saved branch outputs.  Errors as
+ * pack3d_forward (PACK3D_ERR_WORKSPACE also for `saved`).
+ */
+int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* k_loc,
+                         const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                         const int32_t* coords, const int32_t* cell_to_pos,
+                         const float* gate_logits, void* out, void* saved, size_t saved_bytes,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of the saved state pack3d_forward_train writes (0 if invalid). */
+size_t pack3d_saved_size(const pack3d_problem* prob);
+
+/*
+ * Backward of the forward: the exact derivatives of out with respect to its
+ * inputs for the upstream gradient dout [N, Hq, 64] (dtype).  The pages state
+ * the forward (notes, overall framework and key designs 1-3) and use it as a
+ * trained block (notes, the loss/training paragraph); the gradients follow
+ * by the chain rule through the gate softmax, the two softmax attentions,
+ * the rotate-before-pool block sums and the rotations.
+ *   dq: dtype [N, Hq, 64]; dk_loc, dv_loc, dk_cmp, dv_cmp: dtype [N, Hkv, 64];
+ *   dgate: fp32, the shape of gate_logits.  No gradient for `a`.
+ * The inputs are those given to pack3d_forward_train, with its `saved`
+ * state (saved_bytes >= pack3d_saved_size()).  workspace: at least
+ * pack3d_backward_workspace_size() bytes, 256-byte aligned, caller-owned.
+ * Supported: bf16 with Hq/Hkv in {4, 8, 16} (else PACK3D_ERR_UNSUPPORTED).
+ * Every sum runs in an order fixed by coordinates, so repacked inputs give
+ * the permuted gradients bit for bit.
+ */
+int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc,
+                    const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
+                    const int32_t* coords, const int32_t* cell_to_pos, const float* gate_logits,
+                    const void* saved, size_t saved_bytes, const void* dout, void* dq,
+                    void* dk_loc, void* dv_loc, void* dk_cmp, void* dv_cmp, float* dgate,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace pack3d_backward needs for this problem (0 if invalid). */
+size_t pack3d_backward_workspace_size(const pack3d_problem* prob);
+
 /* Bytes of workspace pack3d_forward needs for this problem (0 if invalid). */
 size_t pack3d_forward_workspace_size(const pack3d_problem* prob);
 

@@ -356,13 +356,15 @@ def rotate_transpose(x: np.ndarray, coords: np.ndarray,
 def local_attention_backward(q_rot: np.ndarray, k_rot: np.ndarray, v: np.ndarray,
                              coords: np.ndarray, grid: Sequence[int], window: Sequence[int],
                              scale: float, d_out: np.ndarray,
-                             rows: Optional[np.ndarray] = None, chunk: int = 4096):
+                             rows: Optional[np.ndarray] = None, chunk: int = 4096,
+                             q_is_rows: bool = False):
     """Gradients of the local branch for upstream ``d_out`` [N, Hq, D].
 
     Returns ``(dq [R, Hq, D], dk [N, Hkv, D], dv [N, Hkv, D])``: ``dq`` for the
     query rows ``rows`` (default all) and the contributions of those rows to
     every key.  The window is symmetric (u in N(i) iff i in N(u)), so ``dk``
     and ``dv`` are exact at every key whose own window lies inside ``rows``.
+    With ``q_is_rows`` the queries and ``d_out`` are given for those rows only.
     """
     grid = tuple(int(g) for g in grid)
     n = k_rot.shape[0]
@@ -381,8 +383,9 @@ def local_attention_backward(q_rot: np.ndarray, k_rot: np.ndarray, v: np.ndarray
     for s in range(0, len(rows), chunk):
         r = rows[s:s + chunk]
         nr = len(r)
-        qc = np.asarray(q_rot[r], np.float64).reshape(nr, hkv, grp, d)
-        gc = np.asarray(d_out[r], np.float64).reshape(nr, hkv, grp, d)
+        qsel = np.arange(s, s + nr) if q_is_rows else r
+        qc = np.asarray(q_rot[qsel], np.float64).reshape(nr, hkv, grp, d)
+        gc = np.asarray(d_out[qsel], np.float64).reshape(nr, hkv, grp, d)
         ci = coords[r]
         pos = np.zeros((nr, len(offs)), dtype=np.int64)
         valid = np.zeros((nr, len(offs)), dtype=bool)

@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pack3d.h")
@@ -119,3 +120,41 @@ def test_error_string_is_per_call(pk):
     assert pk.pack3d_last_error() != ""
     assert pk.pack3d_forward_workspace_size(_prob(pk)) > 0
     assert pk.pack3d_last_error() == ""
+
+
+def test_training_entry_points_check_arguments_on_the_host(pk):
+    """pack3d_forward_train and pack3d_backward: NULLs, missing or small
+    buffers and unsupported problems are rejected before any launch."""
+    L = pk.LIB
+    p = _prob(pk, n_q_heads=8, n_kv_heads=2)                 # bf16, Hq/Hkv 4
+    b = ctypes.byref(p)
+    big = 10 ** 12
+    fwd = [FAKE] * 5 + [None] + [FAKE] * 4                 # q .. out (a may be NULL)
+    assert L.pack3d_forward_train(b, *fwd[:-1], None, FAKE, big, FAKE, big, None) == -1
+    assert L.pack3d_forward_train(b, *fwd, None, big, FAKE, big, None) == -4
+    assert "saved" in pk.pack3d_last_error()
+    assert L.pack3d_forward_train(b, *fwd, FAKE, 16, FAKE, big, None) == -4
+    assert L.pack3d_forward_train(b, *fwd, FAKE, big, FAKE + 8, big, None) == -4
+    inp = [FAKE] * 5 + [None] + [FAKE] * 3                 # q .. gate
+    outs = [FAKE] * 5 + [FAKE]                             # dq .. dv_cmp, dgate
+    assert L.pack3d_backward(b, *inp, FAKE, big, None, *outs, FAKE, big, None) == -1
+    assert L.pack3d_backward(b, *inp, FAKE, big, FAKE, *outs, None, big, None) == -4
+    assert L.pack3d_backward(b, *inp, FAKE, 16, FAKE, *outs, FAKE, big, None) == -4
+    f32 = _prob(pk, dtype=torch.float32, n_q_heads=8, n_kv_heads=2)
+    assert L.pack3d_backward(ctypes.byref(f32), *inp, FAKE, big, FAKE, *outs, FAKE, big,
+                             None) == -3
+    assert "bf16" in pk.pack3d_last_error()
+    g2 = _prob(pk, n_q_heads=4, n_kv_heads=2)              # Hq/Hkv 2
+    assert L.pack3d_backward(ctypes.byref(g2), *inp, FAKE, big, FAKE, *outs, FAKE, big,
+                             None) == -3
+
+
+def test_training_buffer_sizes_match_layout(pk):
+    p = _prob(pk, grid=(64, 64, 64), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
+    n, hq = 64 ** 3, 8
+    a256 = lambda b: (b + 255) // 256 * 256
+    assert pk.pack3d_saved_size(p) == 2 * a256(n * hq * 64 * 4) + 2 * a256(n * hq * 4)
+    assert pk.pack3d_backward_workspace_size(p) > pk.pack3d_saved_size(p)
+    bad = _prob(pk, head_dim=16)
+    assert pk.pack3d_saved_size(bad) == 0
+    assert pk.pack3d_backward_workspace_size(bad) == 0
