@@ -6,9 +6,12 @@ Q and K_loc, block summaries, local attention, query->summary attention with
 the fused gate), inputs resident in HBM.  Prints ONE JSON line with the
 throughput in tokens/s, the roofline position of the dominant kernel
 (k_global_attn, bf16 MFMA), per-kernel figures, and the fp64 CPU oracle timed
-on a bounded sample of the same workload on this host's cores.
+on a bounded sample of the same workload on this host's cores.  A second leg
+("training") times the training forward plus the backward (all six input
+gradients) on the same inputs with a seeded upstream gradient.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--dense]
+                    [--no-backward]
 """
 
 from __future__ import annotations
@@ -72,6 +75,11 @@ def algorithmic(w: sg.Workload) -> dict:
         "local_flops": 4 * nbr * hq * 64,
         # global: QK^T and PV against all M summaries: 256 flops per (row, summary)
         "global_flops": 4 * n * hq * m * 64,
+        # backward, per (row, key) pair of either branch: recompute S = QK^T,
+        # dP = dO V^T, dQ = dS K, dK = dS^T Q, dV = P^T dO: 5 products of
+        # 2 * 64 flops (the usual 2.5x of the forward's two)
+        "local_bwd_flops": 10 * nbr * hq * 64,
+        "global_bwd_flops": 10 * n * hq * m * 64,
     }
 
 
@@ -102,6 +110,41 @@ def cpu_baseline(w: sg.Workload, inp: sg.Inputs, rows: int) -> dict:
                       f"linearly in query tokens to {whole:.0f} s"}
 
 
+def training_leg(pk, torch, w, inp, dev, dt, fargs, ws, out, args, work, peak_mfma) -> dict:
+    """Training forward (saves both branches' outputs and log-sum-exp) and the
+    backward (dq, dk_loc, dv_loc, dk_cmp, dv_cmp, dgate), timed with events on
+    the launch stream around each call."""
+    print("[bench] training leg: forward_train + backward", file=sys.stderr, flush=True)
+    dout = dev(sg.make_upstream_grad(inp), dt)
+    bws = torch.empty(pk.pack3d_backward_workspace_size(fargs[0]), dtype=torch.uint8,
+                      device="cuda")
+    out_t, saved = pk.pack3d_forward_train(*fargs, workspace=ws, out=out)
+    grads = pk.pack3d_backward(*fargs, saved, dout, workspace=bws)
+    for _ in range(max(args.warmup - 1, 0)):
+        pk.pack3d_forward_train(*fargs, workspace=ws, saved=saved, out=out_t)
+        pk.pack3d_backward(*fargs, saved, dout, workspace=bws, grads=grads)
+    steps = max(args.steps // 2, 1)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record()
+        pk.pack3d_forward_train(*fargs, workspace=ws, saved=saved, out=out_t)
+        e[1].record()
+        pk.pack3d_backward(*fargs, saved, dout, workspace=bws, grads=grads)
+        e[2].record()
+    torch.cuda.synchronize()
+    f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    b_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    bwd_flops = work["local_bwd_flops"] + work["global_bwd_flops"]
+    print(f"[bench] training: forward_train {f_ms:.3f} ms, backward {b_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+    return {"steps": steps, "forward_train_ms": f_ms, "backward_ms": b_ms,
+            "tokens_per_s": w.n_tokens / ((f_ms + b_ms) * 1e-3),
+            "backward_algorithmic_tflop": bwd_flops / 1e12,
+            "backward_tflops": bwd_flops / (b_ms * 1e-3) / 1e12,
+            "backward_frac": bwd_flops / (b_ms * 1e-3) / 1e12 / peak_mfma}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,8 +155,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense", action="store_true",
                     help="also time dense axial-RoPE attention (1x1x1 blocks) on the same inputs")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training leg (forward_train + backward)")
     ap.add_argument("--profile-only", action="store_true",
                     help="for counter runs: a known-size copy probe, then 3 forwards")
+    ap.add_argument("--profile-backward", action="store_true",
+                    help="with --profile-only: 3 training forwards + backwards instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the operator's "
@@ -147,8 +194,15 @@ def main() -> int:
         y = torch.empty_like(x)
         for _ in range(3):
             torch.neg(x, out=y)           # copy probe: reads and writes 256 MiB
-        for _ in range(3):
-            pk.pack3d_forward(*fargs, workspace=ws, out=out)
+        if args.profile_backward:
+            dout = dev(sg.make_upstream_grad(inp), dt)
+            saved, grads = None, None
+            for _ in range(3):
+                _, saved = pk.pack3d_forward_train(*fargs, workspace=ws, saved=saved, out=out)
+                grads = pk.pack3d_backward(*fargs, saved, dout, grads=grads)
+        else:
+            for _ in range(3):
+                pk.pack3d_forward(*fargs, workspace=ws, out=out)
         torch.cuda.synchronize()
         print("[bench] profile-only run done", file=sys.stderr, flush=True)
         return 0
@@ -228,6 +282,10 @@ def main() -> int:
             "ms": dms, "tflops": tfl(dfl, dms), "frac": tfl(dfl, dms) / peak_mfma,
             "speedup_pack3d_vs_dense": dms / ms}
 
+    training = None
+    if not args.no_backward and w.dtype == "bf16":   # the backward takes bf16
+        training = training_leg(pk, torch, w, inp, dev, dt, fargs, ws, out, args, work, peak_mfma)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -255,6 +313,7 @@ def main() -> int:
                      "frac": g_tflops / peak_mfma, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "training": training,
         **extra,
     }
     print(json.dumps(line), flush=True)

@@ -254,6 +254,7 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
     st16(v_l[b] + TL::chunk_off(srow, sch), sv);
     __syncthreads();
     if (t + 1 < nt) load(t + 1, sk, sv);
+    const bool full = (t + 1) * kGKt <= A.m;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       bf16x8 kf[4], vf[4];
@@ -265,11 +266,19 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
         const f32x16 s = contract_dims(kf, qf[cb]);
         const f32x16 dp = contract_dims(vf, df[cb]);
         f32x16 ds;
+        if (full) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = t * kGKt + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          const float p = key < A.m ? __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -lse2[cb])) : 0.0f;
-          ds[v] = p * (dp[v] - ddv[cb]);
+          for (int v = 0; v < 16; ++v)
+            ds[v] = __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -lse2[cb])) * (dp[v] - ddv[cb]);
+        } else {
+          // keys past M: zero rows in LDS, p = 0
+          const int lim = (int)(A.m - t * kGKt) - kb * 32 - 4 * h;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const bool ok = 8 * (v >> 2) + (v & 3) < lim;
+            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -lse2[cb])) : 0.0f;
+            ds[v] = p * (dp[v] - ddv[cb]);
+          }
         }
         dsf[cb][0] = Mma<bf16_t>::p_frag(ds, 0);
         dsf[cb][1] = Mma<bf16_t>::p_frag(ds, 1);

@@ -59,7 +59,7 @@ struct GArgs {
 
 // ---------------------------------------------------------------------------
 // LDS tiles.  bf16: K and V both row-major [64 keys][64 dims], chunk c of key
-// row r stored at chunk c ^ ((r >> 1) & 7) (K, see KLds) or c ^ (2r & 6) (V:
+// row r stored at chunk c ^ sw(r) (K, see KLds) or c ^ (2r & 6) (V:
 // the transposing read takes 4 consecutive keys x 16 dims per 16 lanes).
 // fp32: K as above, V transposed [64 dims][kGVld].
 // ---------------------------------------------------------------------------

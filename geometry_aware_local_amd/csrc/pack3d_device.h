@@ -214,8 +214,13 @@ __device__ __forceinline__ void load_qfrag(QFrag<T>& q, const T* row_h /* row + 
 // gfx950 LDS has 64 four-byte banks (256 bytes) and serves a 128-bit read 16
 // lanes at a time: a bf16 row is 128 bytes, so rows r and r+1 sit in
 // different bank halves and the 8 rows of one parity among 16 consecutive
-// rows need distinct chunk positions (swizzle (r >> 1) & 7); an fp32 row is
-// 256 bytes and 16 consecutive rows need distinct positions (r & 15).
+// rows need distinct chunk positions: the swizzle is a bijection of
+// (r >> 1) & 7.  The same bf16 tiles are also read transposed (the 8-byte
+// transposing read, 32 lanes at a time: rows 4i .. 4i+3, the same 4 aligned
+// chunks of each); rows 4i and 4i+2 then need chunk positions in different
+// 4-chunk halves, so bit 2 of the swizzle follows bit 1 of r:
+// sw(r) = 4 * ((r >> 1) & 1) + ((r >> 2) & 3).  An fp32 row is 256 bytes and
+// 16 consecutive rows need distinct positions (r & 15).
 // V^T: [64 dims][ld] elements, ld = key capacity + 4, so consecutive dims
 // start on different banks.
 // ---------------------------------------------------------------------------
@@ -224,7 +229,7 @@ struct KLds {
   static constexpr int kChunkElems = 16 / sizeof(T);       // elements per 16 B
   static constexpr int kChunks = 64 / kChunkElems;          // chunks per row
   __device__ static __forceinline__ int chunk_off(int row, int chunk) {
-    const int sw = sizeof(T) == 2 ? (row >> 1) & 7 : row & 15;
+    const int sw = sizeof(T) == 2 ? (((row >> 1) & 1) << 2) | ((row >> 2) & 3) : row & 15;
     return row * 64 + ((chunk ^ sw) * kChunkElems);
   }
 };

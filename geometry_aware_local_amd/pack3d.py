@@ -352,17 +352,26 @@ def saved_views(prob: Problem, saved: torch.Tensor) -> dict:
 
 def pack3d_backward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate,
                     saved: torch.Tensor, dout: torch.Tensor,
-                    workspace: Optional[torch.Tensor] = None) -> dict:
+                    workspace: Optional[torch.Tensor] = None,
+                    grads: Optional[dict] = None) -> dict:
     """Gradients of the forward's output for upstream ``dout``: a dict with
     dq [N,Hq,64], dk_loc, dv_loc, dk_cmp, dv_cmp [N,Hkv,64] (input dtype) and
-    dgate (fp32, the gate logits' shape)."""
+    dgate (fp32, the gate logits' shape).  ``grads`` (a dict returned by an
+    earlier call) supplies the output tensors to overwrite."""
     n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
     gshape = (n, hq, 2) if prob.gate_per_head else (n, 2)
     ws = _buffer(pack3d_backward_workspace_size, prob, q.device) if workspace is None else workspace
-    g = {"dq": _empty((n, hq, 64), dt, q)}
-    for name in ("dk_loc", "dv_loc", "dk_cmp", "dv_cmp"):
-        g[name] = _empty((n, hkv, 64), dt, q)
-    g["dgate"] = _empty(gshape, torch.float32, q)
+    if grads is None:
+        g = {"dq": _empty((n, hq, 64), dt, q)}
+        for name in ("dk_loc", "dv_loc", "dk_cmp", "dv_cmp"):
+            g[name] = _empty((n, hkv, 64), dt, q)
+        g["dgate"] = _empty(gshape, torch.float32, q)
+    else:
+        g = grads
+        want = {"dq": (n, hq, 64), "dk_loc": (n, hkv, 64), "dv_loc": (n, hkv, 64),
+                "dk_cmp": (n, hkv, 64), "dv_cmp": (n, hkv, 64), "dgate": gshape}
+        for name, shape in want.items():
+            _ptr(g[name], torch.float32 if name == "dgate" else dt, shape, name)
     _check(LIB.pack3d_backward(
         ctypes.byref(prob), _ptr(q, dt, (n, hq, 64), "q"),
         _ptr(k_loc, dt, (n, hkv, 64), "k_loc"), _ptr(v_loc, dt, (n, hkv, 64), "v_loc"),
