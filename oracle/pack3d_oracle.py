@@ -36,6 +36,18 @@ single constant; the full list with reasons is kept with the design notes):
 * KV groups: query head h reads KV group h // (Hq / Hkv).
 * gate: one 2-way softmax per token (index 0 = local, 1 = compressed), or
   one per token and head when logits are [N, Hq, 2].
+* summary variants (the notes' key design 2 and the summary's contributions:
+  a cheaper summary-centre placement of the rotation, and a coordinate-blind
+  compressed branch named as the missing control):
+  "token"  (default) every cell's key is rotated by R(c_u) before the
+           weighted sum - the exact form;
+  "centre" the weighted sum of the UNROTATED keys is rotated once by
+           R(c^_j), c^_j the geometric centre of the aligned block
+           (origin + (b - 1) / 2 per axis, a half-integer for even extents);
+  "blind"  no rotation on either side of the compressed branch: unrotated
+           keys are pooled and the branch's logits use the unrotated query.
+  Values are pooled the same way in all three; the local branch is
+  unchanged.
 * backward: the pages print no backward; the gradients below are the exact
   derivatives of the forward above (chain rule through the gate, the two
   softmax attentions, the block sums and the rotations) for an upstream
@@ -56,7 +68,10 @@ __all__ = [
     "gate_mix", "forward", "local_window_sizes",
     "rotate_transpose", "local_attention_backward", "global_attention_backward",
     "block_summaries_backward", "gate_backward", "backward",
+    "SUMMARY_MODES", "block_centres",
 ]
+
+SUMMARY_MODES = ("token", "centre", "blind")
 
 
 # ----------------------------------------------------------------------------
@@ -125,25 +140,42 @@ def block_index(coords: np.ndarray, grid: Sequence[int], block: Sequence[int]) -
     return ((c[:, 0] // block[0]) * nby + c[:, 1] // block[1]) * nbx + c[:, 2] // block[2]
 
 
+def block_centres(grid: Sequence[int], block: Sequence[int]) -> np.ndarray:
+    """Geometric centre (z, y, x) of every aligned block, block-raster order:
+    the block's origin plus (b - 1) / 2 on each axis (the summary-centre
+    variant rotates the pooled key there)."""
+    nb = [g // b for g, b in zip(grid, block)]
+    jz, jy, jx = np.meshgrid(*[np.arange(k) for k in nb], indexing="ij")
+    idx = np.stack([jz.ravel(), jy.ravel(), jx.ravel()], axis=1).astype(np.float64)
+    return idx * np.asarray(block, np.float64) + (np.asarray(block, np.float64) - 1.0) / 2.0
+
+
 def block_summaries(k_cmp: np.ndarray, v_cmp: np.ndarray, a: Optional[np.ndarray],
                     coords: np.ndarray, grid: Sequence[int], block: Sequence[int],
                     rope_pairs: Sequence[int] = (11, 11, 10), base: float = 10000.0,
-                    rope_coords: Optional[np.ndarray] = None):
+                    rope_coords: Optional[np.ndarray] = None, mode: str = "token"):
     """k~_j = sum_{u in B_j} a_u R(c_u) k_u and v~_j = sum_{u in B_j} a_u v_u.
 
     ``k_cmp``/``v_cmp`` are ``[N, Hkv, D]`` (K unrotated: the rotation happens
     here, before the weighted sum); ``a`` is ``[N, Hkv]`` or ``None`` for
     uniform ``1/v``.  ``rope_coords`` replaces the coordinates used by the
     rotation only (block membership still follows ``coords``).
+    ``mode`` "centre" instead rotates sum_u a_u k_u once by R(c^_j) (the
+    block's centre, :func:`block_centres`); "blind" leaves it unrotated.
     Returns ``(k_sum, v_sum)``, each ``[Hkv, M, D]`` float64.
     """
+    if mode not in SUMMARY_MODES:
+        raise ValueError(f"summary mode {mode!r}")
     grid, block = tuple(grid), tuple(block)
     if any(g % b for g, b in zip(grid, block)):
         raise ValueError("block must divide the grid")
     n, hkv, d = k_cmp.shape
     vol = int(np.prod(block))
     m = n // vol
-    kr = rotate(k_cmp, coords if rope_coords is None else rope_coords, rope_pairs, base)
+    if mode == "token":
+        kr = rotate(k_cmp, coords if rope_coords is None else rope_coords, rope_pairs, base)
+    else:
+        kr = np.asarray(k_cmp, np.float64)
     w = (np.full((n, hkv), 1.0 / vol) if a is None else np.asarray(a, dtype=np.float64))
     j = block_index(coords, grid, block)
     cell = (np.asarray(coords[:, 0], np.int64) * grid[1] + coords[:, 1]) * grid[2] + coords[:, 2]
@@ -151,6 +183,8 @@ def block_summaries(k_cmp: np.ndarray, v_cmp: np.ndarray, a: Optional[np.ndarray
     srt = np.lexsort((cell, j))
     wk = (w[:, :, None] * kr)[srt].reshape(m, vol, hkv, d).sum(axis=1)
     wv = (w[:, :, None] * np.asarray(v_cmp, np.float64))[srt].reshape(m, vol, hkv, d).sum(axis=1)
+    if mode == "centre":
+        wk = rotate(wk, block_centres(grid, block), rope_pairs, base)
     return np.ascontiguousarray(wk.transpose(1, 0, 2)), np.ascontiguousarray(wv.transpose(1, 0, 2))
 
 
@@ -313,15 +347,22 @@ def forward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits,
         rows = np.asarray(rows, np.int64)
         q_rot = rotate(np.asarray(q)[rows], coords[rows], p.rope_pairs, p.rope_base)
     k_rot = rotate(k_loc, coords, p.rope_pairs, p.rope_base)
+    mode = getattr(p, "summary_mode", "token")
     k_sum, v_sum = block_summaries(k_cmp, v_cmp, a, coords, p.grid, p.block,
-                                   p.rope_pairs, p.rope_base)
+                                   p.rope_pairs, p.rope_base, mode=mode)
+    # the compressed branch's query: rotated, except in the coordinate-blind
+    # variant
+    if mode != "blind":
+        q_cmp = q_rot
+    else:
+        q_cmp = np.asarray(q, np.float64) if rows is None else np.asarray(q, np.float64)[rows]
     o_loc, lse_loc = local_attention(q_rot, k_rot, v_loc, coords, p.grid, p.window, tau, rows,
                                      q_is_rows=rows is not None)
-    o_cmp, lse_cmp = global_attention(q_rot, k_sum, v_sum, tau, q_is_rows=rows is not None)
+    o_cmp, lse_cmp = global_attention(q_cmp, k_sum, v_sum, tau, q_is_rows=rows is not None)
     g = gate_logits if rows is None else np.asarray(gate_logits)[rows]
     out = gate_mix(o_loc, o_cmp, g)
     return dict(out=out, o_loc=o_loc, o_cmp=o_cmp, lse_loc=lse_loc, lse_cmp=lse_cmp,
-                k_sum=k_sum, v_sum=v_sum, q_rot=q_rot, k_rot=k_rot)
+                k_sum=k_sum, v_sum=v_sum, q_rot=q_rot, k_rot=k_rot, q_cmp=q_cmp)
 
 
 # ----------------------------------------------------------------------------
@@ -456,10 +497,12 @@ def global_attention_backward(q_rot: np.ndarray, k_sum: np.ndarray, v_sum: np.nd
 
 def block_summaries_backward(dk_sum: np.ndarray, dv_sum: np.ndarray, a: Optional[np.ndarray],
                              coords: np.ndarray, grid: Sequence[int], block: Sequence[int],
-                             rope_pairs: Sequence[int] = (11, 11, 10), base: float = 10000.0):
+                             rope_pairs: Sequence[int] = (11, 11, 10), base: float = 10000.0,
+                             mode: str = "token"):
     """Gradients of (k~, v~) with respect to (k_cmp, v_cmp): since
     k~_j = sum_{u in B_j} a_u R(c_u) k_u and v~_j = sum a_u v_u,
-    dk_u = a_u R(c_u)^T dk~_j(u) and dv_u = a_u dv~_j(u)."""
+    dk_u = a_u R(c_u)^T dk~_j(u) and dv_u = a_u dv~_j(u).  For the
+    summary-centre variant R(c_u) is R(c^_j(u)); coordinate-blind: no R."""
     hkv, m, d = dk_sum.shape
     n = len(coords)
     vol = int(np.prod(block))
@@ -467,7 +510,15 @@ def block_summaries_backward(dk_sum: np.ndarray, dv_sum: np.ndarray, a: Optional
     j = block_index(coords, grid, block)
     gk = np.asarray(dk_sum, np.float64)[:, j].transpose(1, 0, 2)      # [N, Hkv, D]
     gv = np.asarray(dv_sum, np.float64)[:, j].transpose(1, 0, 2)
-    dk = rotate_transpose(w[:, :, None] * gk, coords, rope_pairs, base)
+    if mode == "token":
+        dk = rotate_transpose(w[:, :, None] * gk, coords, rope_pairs, base)
+    elif mode == "centre":
+        dk = rotate_transpose(w[:, :, None] * gk, block_centres(grid, block)[j], rope_pairs,
+                              base)
+    elif mode == "blind":
+        dk = w[:, :, None] * gk
+    else:
+        raise ValueError(f"summary mode {mode!r}")
     dv = w[:, :, None] * gv
     return dk, dv
 
@@ -504,12 +555,16 @@ def backward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits, d_out,
     dgate, d_loc, d_cmp = gate_backward(gate_logits, d_out, f["o_loc"], f["o_cmp"])
     dq_l, dk_r, dv_loc = local_attention_backward(f["q_rot"], f["k_rot"], v_loc, coords, p.grid,
                                                   p.window, tau, d_loc)
-    dq_c, dk_sum, dv_sum = global_attention_backward(f["q_rot"], f["k_sum"], f["v_sum"], tau,
+    dq_c, dk_sum, dv_sum = global_attention_backward(f["q_cmp"], f["k_sum"], f["v_sum"], tau,
                                                      d_cmp)
-    dq = rotate_transpose(dq_l + dq_c, coords, p.rope_pairs, p.rope_base)
+    mode = getattr(p, "summary_mode", "token")
+    if mode != "blind":
+        dq = rotate_transpose(dq_l + dq_c, coords, p.rope_pairs, p.rope_base)
+    else:       # the compressed branch saw the unrotated query
+        dq = rotate_transpose(dq_l, coords, p.rope_pairs, p.rope_base) + dq_c
     dk_loc = rotate_transpose(dk_r, coords, p.rope_pairs, p.rope_base)
     dk_cmp, dv_cmp = block_summaries_backward(dk_sum, dv_sum, a, coords, p.grid, p.block,
-                                              p.rope_pairs, p.rope_base)
+                                              p.rope_pairs, p.rope_base, mode=mode)
     return dict(dq=dq, dk_loc=dk_loc, dv_loc=dv_loc, dk_cmp=dk_cmp, dv_cmp=dv_cmp,
                 dgate=dgate, dk_sum=dk_sum, dv_sum=dv_sum, d_loc=d_loc, d_cmp=d_cmp,
                 fwd=f)

@@ -125,6 +125,7 @@ class Workload:
     head_dim: int = 64
     rope_pairs: tuple = (11, 11, 10)
     rope_base: float = 10000.0
+    summary_mode: str = "token"   # "token", "centre" or "blind" (compressed-branch variant)
 
     @property
     def n_tokens(self) -> int:
