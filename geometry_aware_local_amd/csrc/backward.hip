@@ -862,11 +862,13 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// k_unrotate: y = R(c)^T x for fp32 x [N, H, 64] -> bf16 y; 8 lanes per
-// token, lane = 16-byte chunk (4 pairs) of every head.
+// k_unrotate: y = R(c)^T x (kRot) or y = x for fp32 x [N, H, 64] -> y of
+// type TO (bf16 output, or fp32 in place); 8 lanes per token, lane = 16-byte
+// chunk (4 pairs) of every head.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_unrotate(const float* __restrict__ x, bf16_t* y,
-                                                  int64_t n, int32_t heads,
+template <bool kRot, typename TO>
+__global__ __launch_bounds__(256) void k_unrotate(const float* x, TO* y, int64_t n,
+                                                  int32_t heads,
                                                   const int32_t* __restrict__ coords,
                                                   RopeTab rt) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -874,22 +876,26 @@ __global__ __launch_bounds__(256) void k_unrotate(const float* __restrict__ x, b
   const int chunk = (int)(gid & 7);
   if (tok >= n) return;
   float sn[4], cs[4];
-  chunk_sincos(rt, chunk, coords[3 * tok], coords[3 * tok + 1], coords[3 * tok + 2], sn, cs);
+  if (kRot)
+    chunk_sincos(rt, chunk, coords[3 * tok], coords[3 * tok + 1], coords[3 * tok + 2], sn, cs);
   for (int hd = 0; hd < heads; ++hd) {
     float v[8];
     load8<float>(x + (tok * heads + hd) * 64 + chunk * 8, v);
+    if (kRot) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x0 = v[2 * i], x1 = v[2 * i + 1];
-      v[2 * i] = cs[i] * x0 + sn[i] * x1;
-      v[2 * i + 1] = cs[i] * x1 - sn[i] * x0;
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = v[2 * i], x1 = v[2 * i + 1];
+        v[2 * i] = cs[i] * x0 + sn[i] * x1;
+        v[2 * i + 1] = cs[i] * x1 - sn[i] * x0;
+      }
     }
-    store8<bf16_t>(y + (tok * heads + hd) * 64 + chunk * 8, v);
+    store8<TO>(y + (tok * heads + hd) * 64 + chunk * 8, v);
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_sum_bwd: dk_cmp[u, g] = a[u, g] R(c_u)^T sum_s dk~_s[g, j(u)],
+// k_sum_bwd: dk_cmp[u, g] = a[u, g] R^T sum_s dk~_s[g, j(u)] with R = R(c_u)
+// (exact form), R(c^_j) (summary centre) or the identity (blind),
 // dv_cmp[u, g] = a[u, g] sum_s dv~_s[g, j(u)] (s = slices of the query
 // stream, summed in order); 8 lanes per token, lane = 16-byte chunk.
 // ---------------------------------------------------------------------------
@@ -905,7 +911,7 @@ __global__ __launch_bounds__(256) void k_sum_bwd(const float* __restrict__ dks,
   const int z = coords[3 * tok], yy = coords[3 * tok + 1], xx = coords[3 * tok + 2];
   const int64_t j = ((int64_t)(z / g.bz) * (g.Y / g.by) + yy / g.by) * (g.X / g.bx) + xx / g.bx;
   float sn[4], cs[4];
-  chunk_sincos(g.rope, chunk, z, yy, xx, sn, cs);
+  summary_sincos(g, chunk, z, yy, xx, sn, cs);
   for (int gr = 0; gr < g.Hkv; ++gr) {
     float sk[8] = {}, sv[8] = {};
     for (int s = 0; s < nsplit; ++s) {
@@ -996,9 +1002,18 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  const dim3 tok_grid((unsigned)((g.N * 8 + 255) / 256));
+  const bool blind = g.summary_mode == PACK3D_SUMMARY_BLIND;
+  if (blind) {
+    // the compressed branch saw the unrotated query: un-rotate the local dq
+    // first (in place, fp32), then add the summary dq
+    hipLaunchKernelGGL((bw::k_unrotate<true, float>), tok_grid, dim3(256), 0, s, b.dq_acc,
+                       b.dq_acc, g.N, g.Hq, b.coords, g.rope);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   {
     bw::GdqArgs A;
-    A.q = (const bf16_t*)b.q_rot;
+    A.q = (const bf16_t*)b.q_cmp;
     A.dco = (const bf16_t*)b.dco;
     A.ks = (const bf16_t*)b.k_sum;
     A.vs = (const bf16_t*)b.v_sum;
@@ -1024,9 +1039,13 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
     hipLaunchKernelGGL(bw::k_glob_dq, dim3((unsigned)blocks), dim3(64 * bw::kGW), 0, s, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // 4. dq = R^T dq_acc
-  hipLaunchKernelGGL(bw::k_unrotate, dim3((unsigned)((g.N * 8 + 255) / 256)), dim3(256), 0, s,
-                     b.dq_acc, (bf16_t*)b.dq, g.N, g.Hq, b.coords, g.rope);
+  // 4. dq = R^T dq_acc (blind: already un-rotated, only rounded to bf16)
+  if (blind)
+    hipLaunchKernelGGL((bw::k_unrotate<false, bf16_t>), tok_grid, dim3(256), 0, s, b.dq_acc,
+                       (bf16_t*)b.dq, g.N, g.Hq, b.coords, g.rope);
+  else
+    hipLaunchKernelGGL((bw::k_unrotate<true, bf16_t>), tok_grid, dim3(256), 0, s, b.dq_acc,
+                       (bf16_t*)b.dq, g.N, g.Hq, b.coords, g.rope);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 5. local dk / dv
   {
@@ -1064,7 +1083,7 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
   const int64_t nsplit = glob_dkv_splits(g);
   {
     bw::GkvArgs A;
-    A.q = (const bf16_t*)b.q_rot;
+    A.q = (const bf16_t*)b.q_cmp;
     A.dco = (const bf16_t*)b.dco;
     A.ks = (const bf16_t*)b.k_sum;
     A.vs = (const bf16_t*)b.v_sum;

@@ -82,6 +82,9 @@ int make_geom(const pack3d_problem* p, Geom* g) {
   if (p->gate_per_head != 0 && p->gate_per_head != 1)
     return fail(PACK3D_ERR_SHAPE, "gate_per_head must be 0 or 1");
   if (!isfinite(p->scale)) return fail(PACK3D_ERR_SHAPE, "scale is not finite");
+  if (p->summary_mode < PACK3D_SUMMARY_TOKEN || p->summary_mode > PACK3D_SUMMARY_BLIND)
+    return fail(PACK3D_ERR_SHAPE, "summary_mode %d unknown (0 token, 1 centre, 2 blind)",
+                p->summary_mode);
 
   g->Z = p->grid[0];
   g->Y = p->grid[1];
@@ -101,6 +104,7 @@ int make_geom(const pack3d_problem* p, Geom* g) {
   g->scale = p->scale > 0.0f ? p->scale : (float)(1.0 / sqrt((double)p->head_dim));
   g->bf16 = p->dtype == PACK3D_BF16;
   g->gate_per_head = p->gate_per_head;
+  g->summary_mode = p->summary_mode;
   // rotary table: pair p = r-th pair of axis a, omega = base^(-r/m_a), stored
   // in turns (omega / 2pi)
   memset(&g->rope, 0, sizeof g->rope);
@@ -355,7 +359,9 @@ int forward_impl(const pack3d_problem* prob, const void* q, const void* k_loc, c
   if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, nullptr, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  e = launch_global_attn(g, q_rot, k_sum, v_sum, g.M, kmax, nullptr, nullptr, o_loc, gate_logits,
+  // the compressed branch's query: rotated, or the input q when it is blind
+  const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? q : q_rot;
+  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, nullptr, nullptr, o_loc, gate_logits,
                          out, s);
   if (e != hipSuccess) return hip_status(e, "k_global_attn(gated)");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
@@ -463,7 +469,8 @@ int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* 
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
   if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, lse_loc, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
-  e = launch_global_attn(g, q_rot, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, nullptr, nullptr,
+  const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? q : q_rot;
+  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, nullptr, nullptr,
                          nullptr, s);
   if (e != hipSuccess) return hip_status(e, "k_global_attn");
   return hip_status(launch_gate_mix(g, o_loc, o_cmp, gate_logits, out, s), "k_gate_mix");
@@ -505,6 +512,7 @@ int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc
   b.lse_loc = (const float*)(sv + sl.lse_loc);
   b.lse_cmp = (const float*)(sv + sl.lse_cmp);
   b.q_rot = ws + w.q_rot;
+  b.q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? q : b.q_rot;
   b.k_rot = ws + w.k_rot;
   b.k_sum = ws + w.k_sum;
   b.v_sum = ws + w.v_sum;

@@ -43,8 +43,8 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 // and the quarter-turn index k selects and signs the pair.  Depends only on
 // (nu, c), so every kernel rotates a given cell identically.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rope_sincos(double nu, int c, float& sn, float& cs) {
-  const double t = nu * (double)c;                      // turns
+__device__ __forceinline__ void rope_sincos(double nu, double c, float& sn, float& cs) {
+  const double t = nu * c;                              // turns
   const double q = rint(4.0 * t);                       // quarter turns
   const float x = (float)((t - 0.25 * q) * 6.283185307179586);
   const int k = ((int)q) & 3;
@@ -70,17 +70,38 @@ __device__ __forceinline__ void rotate8(float* v, const float* sn, const float* 
   }
 }
 
-// cos/sin for the 4 pairs of dim-chunk `chunk` (8 dims) at cell (z, y, x).
-__device__ __forceinline__ void chunk_sincos(const RopeTab& rt, int chunk, int z, int y, int x,
-                                             float* sn, float* cs) {
+// cos/sin for the 4 pairs of dim-chunk `chunk` (8 dims) at point (z, y, x):
+// a lattice cell, or a block centre (half-integers are exact in double).
+__device__ __forceinline__ void chunk_sincos(const RopeTab& rt, int chunk, double z, double y,
+                                             double x, float* sn, float* cs) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int p = chunk * 4 + i;
     if (p < rt.npairs) {
       const int ax = rt.axis[p];
-      const int c = ax == 0 ? z : (ax == 1 ? y : x);
+      const double c = ax == 0 ? z : (ax == 1 ? y : x);
       rope_sincos(rt.nu[p], c, sn[i], cs[i]);
     } else {
+      sn[i] = 0.0f;
+      cs[i] = 1.0f;
+    }
+  }
+}
+
+// The rotation a key summary carries for the token at cell (z, y, x) of
+// block (jz, jy, jx): R(c_u) for the exact form, R(c^_j) at the block's
+// geometric centre for the summary-centre variant, none when blind.
+__device__ __forceinline__ void summary_sincos(const Geom& g, int chunk, int z, int y, int x,
+                                               float* sn, float* cs) {
+  if (g.summary_mode == PACK3D_SUMMARY_TOKEN) {
+    chunk_sincos(g.rope, chunk, z, y, x, sn, cs);
+  } else if (g.summary_mode == PACK3D_SUMMARY_CENTRE) {
+    chunk_sincos(g.rope, chunk, (z / g.bz) * g.bz + 0.5 * (g.bz - 1),
+                 (y / g.by) * g.by + 0.5 * (g.by - 1), (x / g.bx) * g.bx + 0.5 * (g.bx - 1), sn,
+                 cs);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       sn[i] = 0.0f;
       cs[i] = 1.0f;
     }

@@ -34,6 +34,7 @@ struct Geom {
   float scale;                    // softmax scale
   int32_t bf16;                   // 1: bf16 tensors, 0: fp32
   int32_t gate_per_head;
+  int32_t summary_mode;           // pack3d_summary_mode
   RopeTab rope;
 };
 
@@ -77,6 +78,7 @@ struct BwdBuffers {
   const float* o_cmp;          // saved [N, Hq, 64]
   const float* lse_loc;        // saved [N, Hq]
   const float* lse_cmp;        // saved [N, Hq]
+  const void* q_cmp;           // the compressed branch's query (q_rot, or q if blind)
   const void* q_rot;           // workspace: rotated q, k_loc, unscaled summaries
   const void* k_rot;
   const void* k_sum;

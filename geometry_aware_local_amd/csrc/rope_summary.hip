@@ -58,7 +58,9 @@ hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
 // in raster order, 8 per pass; each lane rotates its K chunk by its cell's
 // coordinates (rotation before the weighted sum), weights K and V by a, and
 // accumulates in fp32.  The 8 cell slots are then reduced with a fixed XOR
-// tree, so the summation order depends only on cell positions.
+// tree, so the summation order depends only on cell positions.  The
+// summary-centre variant rotates the reduced sum once at the block centre
+// instead; the coordinate-blind variant does not rotate.
 // ---------------------------------------------------------------------------
 constexpr int kSumWaves = 4;
 constexpr int kMaxPasses = kMaxBlockVol / 8;
@@ -79,6 +81,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
   const int jx = (int)(j % nbx), jy = (int)((j / nbx) % nby), jz = (int)(j / ((int64_t)nbx * nby));
   const int passes = (g.bvol + 7) >> 3;
   const float uniform = 1.0f / (float)g.bvol;
+  const bool per_cell = g.summary_mode == PACK3D_SUMMARY_TOKEN;
 
   // positions and rotations of the lane's cells (one per pass)
   int64_t pos[kMaxPasses];
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
         const int ux = u % g.bx, uy = (u / g.bx) % g.by, uz = u / (g.bx * g.by);
         const int z = jz * g.bz + uz, y = jy * g.by + uy, x = jx * g.bx + ux;
         pos[p] = c2p[((int64_t)z * g.Y + y) * g.X + x];
-        chunk_sincos(g.rope, chunk, z, y, x, sn[p], cs[p]);
+        if (per_cell) chunk_sincos(g.rope, chunk, z, y, x, sn[p], cs[p]);
       }
     }
   }
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
         load8<T>(kc + row, kv);
         load8<T>(vc + row, vv);
         const float w = a ? a[pos[p] * g.Hkv + grp] : uniform;
-        rotate8(kv, sn[p], cs[p]);
+        if (per_cell) rotate8(kv, sn[p], cs[p]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           ak[i] += w * kv[i];
@@ -124,6 +127,11 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
         ak[i] += __shfl_xor(ak[i], off);
         av[i] += __shfl_xor(av[i], off);
       }
+    }
+    if (g.summary_mode == PACK3D_SUMMARY_CENTRE) {
+      float csn[4], ccs[4];
+      summary_sincos(g, chunk, jz * g.bz, jy * g.by, jx * g.bx, csn, ccs);
+      rotate8(ak, csn, ccs);
     }
     float n2 = 0.0f;
 #pragma unroll

@@ -28,6 +28,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpack3d.so")
 
 PACK3D_F32, PACK3D_BF16 = 0, 1
+SUMMARY_MODES = ("token", "centre", "blind")      # pack3d_summary_mode 0, 1, 2
 PACK3D_FORWARD_STAGES = 6
 FORWARD_STAGE_NAMES = ("rope(q)", "rope(k_loc)", "block_summary", "kmax", "local_attn",
                        "global_attn+gate")
@@ -63,6 +64,7 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("gate_per_head", ctypes.c_int32),
+        ("summary_mode", ctypes.c_int32),
     ]
 
     @property
@@ -117,7 +119,10 @@ def make_problem(grid: Sequence[int], n_q_heads: int, n_kv_heads: int,
                  window: Sequence[int] = (3, 7, 7), block: Sequence[int] = (1, 4, 4),
                  dtype: torch.dtype = torch.bfloat16, rope_pairs: Sequence[int] = (11, 11, 10),
                  rope_base: float = 10000.0, scale: float = 0.0, head_dim: int = 64,
-                 gate_per_head: bool = False) -> Problem:
+                 gate_per_head: bool = False, summary_mode="token") -> Problem:
+    """``summary_mode``: "token" (rotation before the block sum, the exact
+    form), "centre" (pooled keys rotated at the block centre) or "blind"
+    (no rotation in the compressed branch), or the matching int 0/1/2."""
     p = Problem()
     p.grid[:] = list(grid)
     p.n_q_heads, p.n_kv_heads, p.head_dim = n_q_heads, n_kv_heads, head_dim
@@ -127,6 +132,8 @@ def make_problem(grid: Sequence[int], n_q_heads: int, n_kv_heads: int,
     p.rope_base, p.scale = rope_base, scale
     p.dtype = PACK3D_BF16 if dtype == torch.bfloat16 else PACK3D_F32
     p.gate_per_head = int(gate_per_head)
+    p.summary_mode = (summary_mode if isinstance(summary_mode, int)
+                      else SUMMARY_MODES.index(summary_mode))
     return p
 
 

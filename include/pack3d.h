@@ -59,6 +59,24 @@ typedef enum pack3d_status {
 typedef enum pack3d_dtype { PACK3D_F32 = 0, PACK3D_BF16 = 1 } pack3d_dtype;
 
 /*
+ * Compressed-branch variants (notes, key design 2: rotating every key before
+ * the block sum is the exact form; summary, contributions and findings: a
+ * cheaper summary-centre placement, and a coordinate-blind compressed branch
+ * as the missing control).
+ *   TOKEN   k~_j = sum_u a_u R(c_u) k_u; the branch's query is R(c_i) q_i.
+ *   CENTRE  k~_j = R(c^_j) sum_u a_u k_u, c^_j the block's geometric centre
+ *           (origin + (b - 1)/2 per axis, half-integer for even extents);
+ *           the branch's query is R(c_i) q_i.
+ *   BLIND   k~_j = sum_u a_u k_u and the branch's query is the unrotated q_i.
+ * Values are pooled the same way in all three; the local branch is unchanged.
+ */
+typedef enum pack3d_summary_mode {
+  PACK3D_SUMMARY_TOKEN = 0,
+  PACK3D_SUMMARY_CENTRE = 1,
+  PACK3D_SUMMARY_BLIND = 2
+} pack3d_summary_mode;
+
+/*
  * One operator instance.
  *   grid[3]        lattice extents Z, Y, X (all >= 1); N = Z*Y*X < 2^31.
  *   n_q_heads      Hq; n_kv_heads Hkv; Hq % Hkv == 0 (query head h reads KV
@@ -79,6 +97,7 @@ typedef enum pack3d_dtype { PACK3D_F32 = 0, PACK3D_BF16 = 1 } pack3d_dtype;
  *   scale          softmax scale; <= 0 selects 1/sqrt(head_dim).
  *   dtype          pack3d_dtype of q/k/v/out.
  *   gate_per_head  0: gate logits are [N, 2]; 1: [N, Hq, 2].
+ *   summary_mode   pack3d_summary_mode; 0 (TOKEN) is the pages' exact form.
  */
 typedef struct pack3d_problem {
   int32_t grid[3];
@@ -92,6 +111,7 @@ typedef struct pack3d_problem {
   float scale;
   int32_t dtype;
   int32_t gate_per_head;
+  int32_t summary_mode;
 } pack3d_problem;
 
 /*
@@ -111,6 +131,8 @@ int pack3d_rope(const pack3d_problem* prob, const void* x, void* y, int32_t n_he
  * B_j is the j-th aligned block in block-raster order,
  *   j = ((z/bz)*(Y/by) + y/by)*(X/bx) + x/bx.
  * k_cmp is NOT rotated (the rotation happens inside, before the sum).
+ * With summary_mode CENTRE the weighted sum of the unrotated keys is rotated
+ * once by R(c^_j); with BLIND it is not rotated.
  * k_cmp, v_cmp: dtype [N, Hkv, head_dim].  a: fp32 [N, Hkv] or NULL for the
  * uniform 1/v (normalisation is the caller's contract).  cell_to_pos: int32
  * [N].  k_sum, v_sum: dtype [Hkv, M, head_dim], rounded once from fp32.
@@ -138,6 +160,8 @@ int pack3d_local_attn(const pack3d_problem* prob, const void* q_rot, const void*
  *   o_cmp[i, h] = sum_{j < m} softmax_j(scale <q_rot[i,h], k_sum[g,j]>) v_sum[g,j]
  * q_rot: dtype [N, Hq, head_dim]; k_sum, v_sum: dtype [Hkv, m, head_dim]
  * (m >= 1 is explicit, so m = N with 1x1x1 blocks is dense attention).
+ * The query operand is the compressed branch's query: rotated for TOKEN and
+ * CENTRE, the unrotated q for BLIND (the caller passes it).
  * o_cmp: fp32 [N, Hq, head_dim]; lse_cmp: fp32 [N, Hq] or NULL.
  */
 int pack3d_global_attn(const pack3d_problem* prob, const void* q_rot, const void* k_sum,

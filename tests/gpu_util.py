@@ -35,6 +35,7 @@ def dev(x, dtype=None):
 
 
 def problem(pk, w: sg.Workload, **kw):
+    kw.setdefault("summary_mode", w.summary_mode)
     return pk.make_problem(w.grid, w.n_q_heads, w.n_kv_heads, w.window, w.block, tdtype(w),
                            w.rope_pairs, w.rope_base, **kw)
 

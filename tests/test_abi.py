@@ -65,6 +65,8 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
     (dict(rope_pairs=(11, 11, 11)), -2, "rope_pairs"),
     (dict(rope_base=-1.0), -2, "rope_base"),
     (dict(grid=(2048, 1024, 1024)), -2, "int32"),
+    (dict(summary_mode=3), -2, "summary_mode"),
+    (dict(summary_mode=-1), -2, "summary_mode"),
 ])
 def test_bad_problems_are_rejected_on_the_host(pk, kw, code, text):
     p = _prob(pk, **kw)
@@ -72,6 +74,18 @@ def test_bad_problems_are_rejected_on_the_host(pk, kw, code, text):
     assert rc == code
     assert text in pk.pack3d_last_error()
     assert pk.pack3d_forward_workspace_size(p) == 0
+
+
+def test_problem_struct_matches_the_header(pk):
+    """The ctypes mirror has the header's fields in order (the last one is
+    the compressed-branch variant) and the C struct's size."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct pack3d_problem \{(.*?)\} pack3d_problem;", text, re.S)
+    fields = re.findall(r"^\s*\w+\s+(\w+)(?:\[\d\])?;", body.group(1), re.M)
+    assert fields == [f[0] for f in pk.Problem._fields_]
+    assert ctypes.sizeof(pk.Problem) == 88
+    assert [pk.make_problem((1, 4, 4), 2, 1, summary_mode=m).summary_mode
+            for m in pk.SUMMARY_MODES] == [0, 1, 2]
 
 
 def test_null_arguments_are_rejected(pk):
