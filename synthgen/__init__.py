@@ -31,7 +31,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-PACKINGS = ("raster", "morton", "block", "random")
+PACKINGS = ("raster", "morton", "block", "block_morton", "random")
 
 
 # ----------------------------------------------------------------------------
@@ -66,6 +66,8 @@ def packing_order(grid: Sequence[int], kind: str, seed: int = 0,
     * ``morton``: stable sort of the cells by their Morton key.
     * ``block``: block-contiguous (raster_block): blocks of shape ``block`` in
       raster order, raster order inside each block.
+    * ``block_morton``: the two-level layout: blocks of shape ``block`` in
+      Morton order of their block indices, raster order inside each block.
     * ``random``: ``default_rng(seed + 100).permutation(N)``.
     """
     n = int(np.prod(grid))
@@ -80,6 +82,11 @@ def packing_order(grid: Sequence[int], kind: str, seed: int = 0,
         bid = ((cells[:, 0] // bz) * nby + cells[:, 1] // by) * nbx + cells[:, 2] // bx
         inner = ((cells[:, 0] % bz) * by + cells[:, 1] % by) * bx + cells[:, 2] % bx
         return np.lexsort((inner, bid)).astype(np.int64)
+    if kind == "block_morton":
+        bz, by, bx = block
+        bidx = np.stack([cells[:, 0] // bz, cells[:, 1] // by, cells[:, 2] // bx], axis=1)
+        inner = ((cells[:, 0] % bz) * by + cells[:, 1] % by) * bx + cells[:, 2] % bx
+        return np.lexsort((inner, _morton_key(bidx))).astype(np.int64)
     if kind == "random":
         return np.random.default_rng(seed + 100).permutation(n).astype(np.int64)
     raise ValueError(f"unknown packing {kind!r}")
@@ -101,12 +108,24 @@ def packing(grid: Sequence[int], kind: str, seed: int = 0,
 # ----------------------------------------------------------------------------
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    """Round float32 values to the nearest bf16 (ties to even); returns float32.
+
+    Works in chunks of 2^24 values, so multi-gigabyte tensors need no more
+    than one extra chunk of scratch memory.  Finite inputs: the 32-bit
+    carry of the rounding increment can only wrap for NaN bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
-    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+    out = np.empty_like(x)
+    src, dst = x.reshape(-1).view(np.uint32), out.reshape(-1).view(np.uint32)
+    step = 1 << 24
+    for i in range(0, src.size, step):
+        u = src[i:i + step]
+        r = dst[i:i + step]
+        np.right_shift(u, np.uint32(16), out=r)
+        np.bitwise_and(r, np.uint32(1), out=r)
+        r += u
+        r += np.uint32(0x7FFF)
+        r &= np.uint32(0xFFFF0000)
+    return out
 
 
 @dataclasses.dataclass(frozen=True)
@@ -150,6 +169,11 @@ WORKLOADS = {
                                      (3, 7, 7), (1, 4, 4), "bf16", "softmax", 2),
     "block_bf16_64x64x64": Workload("block_bf16_64x64x64", (64, 64, 64), "block", 8, 2,
                                     (3, 7, 7), (1, 4, 4), "bf16", "softmax", 3),
+    # reach: 4M and 8M tokens (the pages' query-tiled systems-reach sizes)
+    "reach_bf16_64x256x256": Workload("reach_bf16_64x256x256", (64, 256, 256), "block", 8, 2,
+                                      (3, 7, 7), (1, 4, 4), "bf16", "softmax", 6),
+    "reach_bf16_128x256x256": Workload("reach_bf16_128x256x256", (128, 256, 256), "block", 8,
+                                       2, (3, 7, 7), (1, 4, 4), "bf16", "softmax", 7),
     "random_bf16_64x128x128": Workload("random_bf16_64x128x128", (64, 128, 128), "random", 8, 2,
                                        (3, 7, 7), (1, 4, 4), "bf16", "softmax", 4),
 }
@@ -198,18 +222,22 @@ class Inputs:
                       take(self.v_cmp), take(self.a), take(self.gate))
 
 
-def make_inputs(w: Workload, explicit_uniform: bool = False) -> Inputs:
+def make_inputs(w: Workload, explicit_uniform: bool = False, progress=None) -> Inputs:
     """Draw a workload's inputs (see the module docstring for the recipe).
 
     With ``weights == "uniform"`` the weights are ``None`` (the operator's
     uniform ``1/v`` default) unless ``explicit_uniform`` asks for the array.
+    ``progress`` (optional callable) is told after each tensor is drawn.
     """
     n, hq, hkv, d = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim
     rng = np.random.default_rng(w.seed)
+    say = progress or (lambda *a: None)
 
     def draw(*shape):
         t = rng.standard_normal(shape, dtype=np.float32)
-        return round_to_bf16(t) if w.dtype == "bf16" else t
+        t = round_to_bf16(t) if w.dtype == "bf16" else t
+        say(f"  drew {shape}")
+        return t
 
     q = draw(n, hq, d)
     k_loc = draw(n, hkv, d)
@@ -226,7 +254,9 @@ def make_inputs(w: Workload, explicit_uniform: bool = False) -> Inputs:
         a = None
     order, coords, c2p = packing(w.grid, w.packing, w.seed, w.block)
     take = lambda t: None if t is None else np.ascontiguousarray(t[order])
-    return Inputs(w, order, coords, c2p, take(q), take(k_loc), take(v_loc), take(k_cmp),
+    q = take(q)
+    say("  packed q")
+    return Inputs(w, order, coords, c2p, q, take(k_loc), take(v_loc), take(k_cmp),
                   take(v_cmp), take(a), take(gate))
 
 

@@ -129,7 +129,7 @@ def test_backward_is_packing_equivariant_bitwise(pk):
     w = C5_SMALL
     inp = sg.make_inputs(w)
     res = {}
-    for kind in ("block", "raster", "random", "morton"):
+    for kind in ("block", "raster", "random", "morton", "block_morton"):
         x = inp.repacked(kind) if kind != w.packing else inp
         dout = sg.make_upstream_grad(x)
         _say("backward equivariance", kind)

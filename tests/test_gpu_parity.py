@@ -5,6 +5,8 @@ from ``oracle/`` only.  Small workloads are compared element by element in
 full; the 262 144- and 1 048 576-token workloads on sampled query rows.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -232,6 +234,42 @@ def test_forward_262k_block_sampled(pk):
     _check_forward(pk, BLOCK, inp, _rows(BLOCK, 1024, seed=2))
 
 
+def _reach(pk, w, nrows):
+    """The forward at reach sizes: 4 194 304 tokens (M = 262 144) and
+    8 388 608 tokens (M = 524 288; element offsets of q pass 2^32), checked
+    on sampled rows (the oracle builds every summary)."""
+    _say("forward reach", w.name, "generating inputs")
+    inp = sg.make_inputs(w, progress=_say)
+    rows = _rows(w, nrows, seed=4)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    _say("  gpu forward")
+    out = pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"],
+                            d["coords"], d["cell_to_pos"], d["gate"])
+    got = gu.host(out[torch.from_numpy(rows).cuda()])
+    del out, d
+    torch.cuda.empty_cache()
+    _say("  oracle on", len(rows), "rows")
+    ref = orc.forward(w, inp.q, inp.k_loc, inp.v_loc, inp.k_cmp, inp.v_cmp, inp.a, inp.coords,
+                      inp.gate, rows=rows)
+    assert gu.max_abs(got, ref["out"]) <= gu.ABS_TOL["bf16"]
+
+
+REACH = pytest.mark.skipif(os.environ.get("PACK3D_REACH") != "1",
+                           reason="reach sizes take minutes of host time for the inputs and "
+                                  "the oracle's summaries; set PACK3D_REACH=1")
+
+
+@REACH
+def test_forward_4m_reach_sampled(pk):
+    _reach(pk, W["reach_bf16_64x256x256"], 64)
+
+
+@REACH
+def test_forward_8m_reach_sampled(pk):
+    _reach(pk, W["reach_bf16_128x256x256"], 64)
+
+
 def test_forward_1m_random_sampled(pk):
     _say("forward", RANDOM.name)
     inp = sg.make_inputs(RANDOM)
@@ -256,14 +294,14 @@ def test_packing_equivariance(pk, w):
     base = sg.make_inputs(w.with_(packing="raster"))
     prob = gu.problem(pk, w)
     outs = {}
-    for kind in ("raster", "block", "random", "morton"):
+    for kind in ("raster", "block", "random", "morton", "block_morton"):
         inp = base if kind == "raster" else base.repacked(kind)
         d = gu.device_inputs(inp)
         out = pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"],
                                 d["a"], d["coords"], d["cell_to_pos"], d["gate"])
         back = torch.from_numpy(inp.cell_to_pos[base.order].astype(np.int64)).cuda()
         outs[kind] = out[back].float()
-    for kind in ("block", "random", "morton"):
+    for kind in ("block", "random", "morton", "block_morton"):
         diff = (outs[kind] - outs["raster"]).abs().max().item()
         assert diff <= 1e-6, (kind, diff)
         assert torch.equal(outs[kind], outs["raster"]), kind

@@ -292,7 +292,7 @@ def test_packing_equivariance(wname):
     w = sg.WORKLOADS.get(wname) or _small(grid=(4, 8, 12), window=(3, 7, 7))
     base = sg.make_inputs(w.with_(packing="raster"))
     ref = _fwd(base)
-    for kind in ("morton", "block", "random"):
+    for kind in ("morton", "block", "block_morton", "random"):
         inp = base.repacked(kind)
         r = _fwd(inp)
         back = inp.cell_to_pos[base.order]   # packed position of each raster cell
@@ -384,6 +384,16 @@ def test_packings_are_bijections_and_morton_is_z_order():
     _, coords, _ = sg.packing((1, 4, 8), "block")
     assert [tuple(c[1:]) for c in coords[:5]] == [(0, 0), (0, 1), (0, 2), (0, 3), (1, 0)]
     assert tuple(coords[16][1:]) == (0, 4)
+    # two-level block-Morton: 1x2x2 blocks of a 1x4x4 lattice visited in z
+    # order of their block indices (0,0), (0,1), (1,0), (1,1), raster inside
+    _, coords, _ = sg.packing((1, 4, 4), "block_morton", block=(1, 2, 2))
+    want = [(0, 0), (0, 1), (1, 0), (1, 1), (0, 2), (0, 3), (1, 2), (1, 3),
+            (2, 0), (2, 1), (3, 0), (3, 1), (2, 2), (2, 3), (3, 2), (3, 3)]
+    assert [tuple(c[1:]) for c in coords] == want
+    _, coords, _ = sg.packing((1, 8, 8), "block_morton", block=(1, 4, 4))
+    assert [tuple(c[1:]) for c in coords[:5]] == [(0, 0), (0, 1), (0, 2), (0, 3), (1, 0)]
+    assert [tuple(c[1:]) for c in coords[16:32:15]] == [(0, 4), (3, 7)]
+    assert tuple(coords[32][1:]) == (4, 0)
 
 
 def test_bf16_rounding_is_nearest_even():
@@ -391,6 +401,10 @@ def test_bf16_rounding_is_nearest_even():
     got = sg.round_to_bf16(x)
     want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(got, want)
+    # across chunk boundaries and with a multi-dimensional shape
+    y = np.random.default_rng(0).standard_normal((3, (1 << 23) + 5), dtype=np.float32)
+    assert np.array_equal(sg.round_to_bf16(y),
+                          torch.from_numpy(y).to(torch.bfloat16).to(torch.float32).numpy())
 
 
 def test_sampled_rows_equal_full_rows():
