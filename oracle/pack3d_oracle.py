@@ -48,6 +48,14 @@ single constant; the full list with reasons is kept with the design notes):
            keys are pooled and the branch's logits use the unrotated query.
   Values are pooled the same way in all three; the local branch is
   unchanged.
+* the layer around the operator (notes, flowchart nodes B and G, and key
+  design 1's q = R(c) W_Q LN(h), k^b = R(c) W_K^b LN(h), v^b = W_V^b LN(h)):
+  pre-norm LayerNorm over the model width with learned scale and shift and
+  eps = 1e-5 (biased variance); the five projections are bias-free and
+  stacked in one weight [Hq*D + 4*Hkv*D, C] in the order Q, K_loc, V_loc,
+  K_cmp, V_cmp; the block returns h + O W_O^T with a bias-free W_O
+  [C, Hq*D] applied to the heads' gated outputs concatenated (the
+  feed-forward network after it is not part of the operator).
 * backward: the pages print no backward; the gradients below are the exact
   derivatives of the forward above (chain rule through the gate, the two
   softmax attentions, the block sums and the rotations) for an upstream
@@ -69,6 +77,7 @@ __all__ = [
     "rotate_transpose", "local_attention_backward", "global_attention_backward",
     "block_summaries_backward", "gate_backward", "backward",
     "SUMMARY_MODES", "block_centres",
+    "layer_norm", "qkv_projection", "layer_forward",
 ]
 
 SUMMARY_MODES = ("token", "centre", "blind")
@@ -568,3 +577,60 @@ def backward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits, d_out,
     return dict(dq=dq, dk_loc=dk_loc, dv_loc=dv_loc, dk_cmp=dk_cmp, dv_cmp=dv_cmp,
                 dgate=dgate, dk_sum=dk_sum, dv_sum=dv_sum, d_loc=d_loc, d_cmp=d_cmp,
                 fwd=f)
+
+
+# ----------------------------------------------------------------------------
+# The layer around the operator (papernotes.org notes, flowchart node B
+# "linear projection and layer normalisation produce Q, K_loc, V_loc, K_cmp,
+# V_cmp" and node G "residual output"; key design 1 writes the projections as
+# W LN(h))
+# ----------------------------------------------------------------------------
+
+def layer_norm(h: np.ndarray, gamma: Optional[np.ndarray], beta: Optional[np.ndarray],
+               eps: float = 1e-5) -> np.ndarray:
+    """(h - mean) / sqrt(var + eps) * gamma + beta over the last axis, with the
+    biased variance; gamma / beta None mean 1 / 0."""
+    h = np.asarray(h, np.float64)
+    mu = h.mean(axis=-1, keepdims=True)
+    var = ((h - mu) ** 2).mean(axis=-1, keepdims=True)
+    y = (h - mu) / np.sqrt(var + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma, np.float64)
+    if beta is not None:
+        y = y + np.asarray(beta, np.float64)
+    return y
+
+
+def qkv_projection(x: np.ndarray, w_qkv: np.ndarray, n_q_heads: int, n_kv_heads: int,
+                   head_dim: int = 64):
+    """The five bias-free projections x W^T, split in the order Q, K_loc,
+    V_loc, K_cmp, V_cmp and shaped per head: ``(q [N, Hq, D], k_loc, v_loc,
+    k_cmp, v_cmp [N, Hkv, D])``."""
+    y = np.asarray(x, np.float64) @ np.asarray(w_qkv, np.float64).T
+    n = y.shape[0]
+    sizes = [n_q_heads * head_dim] + [n_kv_heads * head_dim] * 4
+    if y.shape[1] != sum(sizes):
+        raise ValueError("w_qkv rows must be Hq*D + 4*Hkv*D")
+    out, off = [], 0
+    for sz in sizes:
+        out.append(y[:, off:off + sz].reshape(n, sz // head_dim, head_dim))
+        off += sz
+    return tuple(out)
+
+
+def layer_forward(p, h, gamma, beta, w_qkv, w_o, a, coords, gate_logits, eps: float = 1e-5,
+                  rows: Optional[np.ndarray] = None, scale: Optional[float] = None) -> dict:
+    """h' = h + O W_O^T with O the operator's gated output on the projections
+    of LN(h) (concatenated over heads).  ``h`` is ``[N, C]`` in packed order;
+    with ``rows`` only those tokens' outputs are computed (every key and
+    summary is still built)."""
+    x = layer_norm(h, gamma, beta, eps)
+    q, k_loc, v_loc, k_cmp, v_cmp = qkv_projection(x, w_qkv, p.n_q_heads, p.n_kv_heads,
+                                                   p.head_dim)
+    f = forward(p, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, gate_logits, rows=rows,
+                scale=scale)
+    o = f["out"].reshape(f["out"].shape[0], -1)
+    hr = np.asarray(h, np.float64) if rows is None else np.asarray(h, np.float64)[rows]
+    out = hr + o @ np.asarray(w_o, np.float64).T
+    return dict(out=out, x=x, q=q, k_loc=k_loc, v_loc=v_loc, k_cmp=k_cmp, v_cmp=v_cmp,
+                o=o, fwd=f)

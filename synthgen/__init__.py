@@ -272,3 +272,35 @@ def make_upstream_grad(inp: Inputs, seed_offset: int = 200) -> np.ndarray:
         g = round_to_bf16(g)
     # inp.order[i] is the raster cell at packed position i
     return np.ascontiguousarray(g[inp.order])
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """The layer around the operator: hidden states and weights (float32 host
+    arrays; bf16-rounded for bf16 workloads except the LayerNorm affine)."""
+    h: np.ndarray            # [N, C] in the operator inputs' packing
+    gamma: np.ndarray        # [C] fp32
+    beta: np.ndarray         # [C] fp32
+    w_qkv: np.ndarray        # [Hq*D + 4*Hkv*D, C]
+    w_o: np.ndarray          # [C, Hq*D]
+
+
+def make_layer_inputs(inp: Inputs, width: Optional[int] = None,
+                      seed_offset: int = 300) -> LayerInputs:
+    """Hidden states h ~ N(0, 1) drawn per lattice cell in raster order and
+    placed in ``inp``'s packing; gamma = 1 + 0.1 N(0, 1), beta = 0.1 N(0, 1);
+    W_qkv ~ N(0, 1/C) (so the projections are ~N(0, 1) like the operator's
+    own inputs) and W_O ~ N(0, 1/(Hq*D)), all from ``default_rng(seed +
+    seed_offset)``.  The model width C defaults to Hq * D."""
+    w = inp.workload
+    c = width or w.n_q_heads * w.head_dim
+    rng = np.random.default_rng(w.seed + seed_offset)
+    rnd = (lambda t: round_to_bf16(t)) if w.dtype == "bf16" else (lambda t: t)
+    h = rnd(rng.standard_normal((w.n_tokens, c), dtype=np.float32))
+    gamma = (1.0 + 0.1 * rng.standard_normal(c)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(c)).astype(np.float32)
+    cout = (w.n_q_heads + 4 * w.n_kv_heads) * w.head_dim
+    w_qkv = rnd((rng.standard_normal((cout, c)) / np.sqrt(c)).astype(np.float32))
+    w_o = rnd((rng.standard_normal((c, w.n_q_heads * w.head_dim))
+               / np.sqrt(w.n_q_heads * w.head_dim)).astype(np.float32))
+    return LayerInputs(np.ascontiguousarray(h[inp.order]), gamma, beta, w_qkv, w_o)
