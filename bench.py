@@ -8,10 +8,12 @@ throughput in tokens/s, the roofline position of the dominant kernel
 (k_global_attn, bf16 MFMA), per-kernel figures, and the fp64 CPU oracle timed
 on a bounded sample of the same workload on this host's cores.  A second leg
 ("training") times the training forward plus the backward (all six input
-gradients) on the same inputs with a seeded upstream gradient.
+gradients) on the same inputs with a seeded upstream gradient, and a third
+("layer") the layer around the operator: LayerNorm + the five projections
+with RoPE, the operator, the output projection + residual (width Hq*64).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--dense]
-                    [--no-backward]
+                    [--no-backward] [--no-layer] [--summary-mode MODE]
 """
 
 from __future__ import annotations
@@ -145,6 +147,62 @@ def training_leg(pk, torch, w, inp, dev, dt, fargs, ws, out, args, work, peak_mf
             "backward_frac": bwd_flops / (b_ms * 1e-3) / 1e12 / peak_mfma}
 
 
+def layer_leg(pk, torch, w, inp, fargs, args, peak_mfma) -> dict:
+    """The layer around the operator on the same lattice: width C = Hq*64,
+    h and the weights from synthgen.make_layer_inputs; timed with events on
+    the launch stream around the whole layer and around its two projections
+    (the split entry points, run separately)."""
+    print("[bench] layer leg", file=sys.stderr, flush=True)
+    prob, coords, c2p, a, gate = fargs[0], fargs[7], fargs[8], fargs[6], fargs[9]
+    L = sg.make_layer_inputs(inp)
+    bf = torch.bfloat16
+    h = torch.from_numpy(L.h).to(bf).cuda()
+    gamma, beta = torch.from_numpy(L.gamma).cuda(), torch.from_numpy(L.beta).cuda()
+    w_qkv, w_o = torch.from_numpy(L.w_qkv).to(bf).cuda(), torch.from_numpy(L.w_o).to(bf).cuda()
+    n, c = w.n_tokens, L.h.shape[1]
+    ws = torch.empty(pk.pack3d_layer_workspace_size(prob, c), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(h)
+    run = lambda: pk.pack3d_layer_forward(prob, h, gamma, beta, w_qkv, w_o, a, coords, c2p, gate,
+                                          workspace=ws, out=out)
+    for _ in range(max(args.warmup, 1)):
+        run()
+    steps = max(args.steps // 2, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the projections alone (split entry points)
+    qkv = pk.pack3d_layernorm_qkv(prob, h, gamma, beta, w_qkv, coords)
+    o = torch.empty((n, w.n_q_heads * 64), dtype=bf, device="cuda").normal_()
+    pk.pack3d_out_proj(prob, o, w_o, h)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        qkv = pk.pack3d_layernorm_qkv(prob, h, gamma, beta, w_qkv, coords)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_qkv = e0.elapsed_time(e1) / steps
+    e0.record()
+    for _ in range(steps):
+        pk.pack3d_out_proj(prob, o, w_o, h)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_out = e0.elapsed_time(e1) / steps
+    cout = (w.n_q_heads + 4 * w.n_kv_heads) * 64
+    fl_qkv, fl_out = 2 * n * c * cout, 2 * n * w.n_q_heads * 64 * c
+    print(f"[bench] layer {ms:.3f} ms (layernorm+qkv {ms_qkv:.3f}, out_proj {ms_out:.3f})",
+          file=sys.stderr, flush=True)
+    del qkv
+    return {"steps": steps, "width": c, "ms": ms, "tokens_per_s": n / (ms * 1e-3),
+            "layernorm_qkv_ms": ms_qkv, "layernorm_qkv_tflops": fl_qkv / (ms_qkv * 1e-3) / 1e12,
+            "out_proj_ms": ms_out, "out_proj_tflops": fl_out / (ms_out * 1e-3) / 1e12,
+            "out_proj_gbs": 3 * n * c * 2 / (ms_out * 1e-3) / 1e9}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +215,10 @@ def main() -> int:
                     help="also time dense axial-RoPE attention (1x1x1 blocks) on the same inputs")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training leg (forward_train + backward)")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the layer leg (LayerNorm + projections, operator, output proj)")
+    ap.add_argument("--summary-mode", default="token", choices=("token", "centre", "blind"),
+                    help="compressed-branch variant (token: the exact rotate-before-sum form)")
     ap.add_argument("--profile-only", action="store_true",
                     help="for counter runs: a known-size copy probe, then 3 forwards")
     ap.add_argument("--profile-backward", action="store_true",
@@ -173,7 +235,7 @@ def main() -> int:
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         return 1
 
-    w = sg.WORKLOADS[args.workload]
+    w = sg.WORKLOADS[args.workload].with_(summary_mode=args.summary_mode)
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     inp = sg.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -183,7 +245,7 @@ def main() -> int:
     k_cmp, v_cmp = dev(inp.k_cmp, dt), dev(inp.v_cmp, dt)
     a, coords, c2p, gate = dev(inp.a), dev(inp.coords), dev(inp.cell_to_pos), dev(inp.gate)
     prob = pk.make_problem(w.grid, w.n_q_heads, w.n_kv_heads, w.window, w.block, dt,
-                           w.rope_pairs, w.rope_base)
+                           w.rope_pairs, w.rope_base, summary_mode=w.summary_mode)
     ws = pk.alloc_workspace(prob, q.device)
     out = torch.empty_like(q)
     n = w.n_tokens
@@ -286,6 +348,10 @@ def main() -> int:
     if not args.no_backward and w.dtype == "bf16":   # the backward takes bf16
         training = training_leg(pk, torch, w, inp, dev, dt, fargs, ws, out, args, work, peak_mfma)
 
+    layer = None
+    if not args.no_layer and w.dtype == "bf16":     # the layer takes bf16
+        layer = layer_leg(pk, torch, w, inp, fargs, args, peak_mfma)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -307,13 +373,14 @@ def main() -> int:
         "config": {"workload": w.name, "grid": list(w.grid), "tokens": n, "packing": w.packing,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": 64,
                    "window": list(w.window), "block": list(w.block), "summaries": w.n_blocks,
-                   "parallelism": "single-gpu"},
+                   "summary_mode": w.summary_mode, "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": "k_global_attn (gated, in the forward)",
                      "achieved": g_tflops, "peak": peak_mfma, "unit": "TFLOP/s",
                      "frac": g_tflops / peak_mfma, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "kernels": kernels,
         "training": training,
+        "layer": layer,
         **extra,
     }
     print(json.dumps(line), flush=True)

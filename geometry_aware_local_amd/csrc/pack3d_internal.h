@@ -100,6 +100,18 @@ struct BwdBuffers {
 bool backward_supported(const Geom& g);
 int64_t glob_dkv_splits(const Geom& g);
 hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s);
+// The layer around the operator (bf16): LayerNorm statistics [N, 2] (mean,
+// 1/sqrt(var + eps)); the stacked projection with LayerNorm applied to its
+// input and RoPE to Q and K_loc (q_raw: unrotated Q as well, nullable); the
+// output projection out = resid + o W_o^T.
+hipError_t launch_ln_stats(const Geom& g, int32_t width, const void* h, float eps, float* stats,
+                           hipStream_t s);
+hipError_t launch_qkv_proj(const Geom& g, int32_t width, const void* h, const float* stats,
+                           const float* gamma, const float* beta, const void* w_qkv,
+                           const int32_t* coords, void* q, void* q_raw, void* k_loc,
+                           void* v_loc, void* k_cmp, void* v_cmp, hipStream_t s);
+hipError_t launch_out_proj(const Geom& g, int32_t width, const void* o, const void* w_o,
+                           const void* resid, void* out, hipStream_t s);
 hipError_t launch_gate_mix(const Geom& g, const float* o_loc, const float* o_cmp,
                            const float* gate, void* out, hipStream_t s);
 hipError_t launch_build_cell_index(const Geom& g, const int32_t* coords, int32_t* c2p,

@@ -40,7 +40,8 @@ EXPORTS = (
     "pack3d_gate_mix", "pack3d_forward", "pack3d_forward_timed", "pack3d_forward_workspace_size",
     "pack3d_build_cell_index", "pack3d_check_packing", "pack3d_last_error",
     "pack3d_backend_info", "pack3d_version", "pack3d_saved_size", "pack3d_forward_train",
-    "pack3d_backward_workspace_size", "pack3d_backward",
+    "pack3d_backward_workspace_size", "pack3d_backward", "pack3d_layernorm_qkv",
+    "pack3d_out_proj", "pack3d_layer_forward", "pack3d_layer_workspace_size",
 )
 
 
@@ -99,6 +100,11 @@ def _load() -> ctypes.CDLL:
         "pack3d_check_packing": [P, V, V, V, V],
         "pack3d_forward_train": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V, SZ, V],
         "pack3d_backward": [P, V, V, V, V, V, V, V, V, V, V, SZ, V, V, V, V, V, V, V, V, SZ, V],
+        "pack3d_layernorm_qkv": [P, I32, V, V, V, ctypes.c_float, V, V, V, V, V, V, V, V, V,
+                                 V],
+        "pack3d_out_proj": [P, I32, V, V, V, V, V],
+        "pack3d_layer_forward": [P, I32, V, V, V, ctypes.c_float, V, V, V, V, V, V, V, V, SZ,
+                                 V],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -108,6 +114,8 @@ def _load() -> ctypes.CDLL:
         getattr(lib, name).argtypes, getattr(lib, name).restype = [P], ctypes.c_size_t
     for name in ("pack3d_last_error", "pack3d_backend_info"):
         getattr(lib, name).argtypes, getattr(lib, name).restype = [], ctypes.c_char_p
+    lib.pack3d_layer_workspace_size.argtypes = [P, I32]
+    lib.pack3d_layer_workspace_size.restype = ctypes.c_size_t
     lib.pack3d_version.argtypes, lib.pack3d_version.restype = [], ctypes.c_int
     return lib
 
@@ -411,3 +419,75 @@ def pack3d_check_packing(prob: Problem, coords: torch.Tensor, cell_to_pos: torch
                                      _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
                                      bad.data_ptr(), _stream(coords.device)))
     return int(bad.item())
+
+
+# --------------------------------------------------------------------------
+# the layer around the operator (bf16): LayerNorm + projections (+ RoPE),
+# output projection + residual, and the whole layer
+# --------------------------------------------------------------------------
+
+def pack3d_layernorm_qkv(prob: Problem, h, gamma, beta, w_qkv, coords, eps: float = 1e-5,
+                         with_q_raw: bool = False) -> dict:
+    """LayerNorm(h) projected by the stacked weight ``w_qkv`` [Hq*64 + 4*Hkv*64,
+    C]: returns q_rot, k_rot (rotated by R(c)), v_loc, k_cmp, v_cmp, the
+    LayerNorm statistics ln_stats [N, 2] and, with ``with_q_raw``, q_raw."""
+    n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
+    width = h.shape[1]
+    out = {"q_rot": _empty((n, hq, 64), dt, h), "k_rot": _empty((n, hkv, 64), dt, h)}
+    for name in ("v_loc", "k_cmp", "v_cmp"):
+        out[name] = _empty((n, hkv, 64), dt, h)
+    out["ln_stats"] = _empty((n, 2), torch.float32, h)
+    if with_q_raw:
+        out["q_raw"] = _empty((n, hq, 64), dt, h)
+    _check(LIB.pack3d_layernorm_qkv(
+        ctypes.byref(prob), width, _ptr(h, dt, (n, width), "h"),
+        _ptr(gamma, torch.float32, (width,), "gamma"), _ptr(beta, torch.float32, (width,), "beta"),
+        eps, _ptr(w_qkv, dt, ((hq + 4 * hkv) * 64, width), "w_qkv"),
+        _ptr(coords, torch.int32, (n, 3), "coords"), out["ln_stats"].data_ptr(),
+        out["q_rot"].data_ptr(), out["q_raw"].data_ptr() if with_q_raw else None,
+        out["k_rot"].data_ptr(), out["v_loc"].data_ptr(), out["k_cmp"].data_ptr(),
+        out["v_cmp"].data_ptr(), _stream(h.device)))
+    return out
+
+
+def pack3d_out_proj(prob: Problem, o, w_o, residual) -> torch.Tensor:
+    """residual + o W_o^T with o [N, Hq*64] (or [N, Hq, 64]), W_o [C, Hq*64]."""
+    n, hq, dt = prob.n_tokens, prob.n_q_heads, prob.torch_dtype
+    width = residual.shape[1]
+    out = _empty((n, width), dt, residual)
+    _check(LIB.pack3d_out_proj(
+        ctypes.byref(prob), width, _ptr(o.reshape(n, hq * 64), dt, (n, hq * 64), "o"),
+        _ptr(w_o, dt, (width, hq * 64), "w_o"), _ptr(residual, dt, (n, width), "residual"),
+        out.data_ptr(), _stream(residual.device)))
+    return out
+
+
+def pack3d_layer_workspace_size(prob: Problem, width: int) -> int:
+    return int(LIB.pack3d_layer_workspace_size(ctypes.byref(prob), width))
+
+
+def pack3d_layer_forward(prob: Problem, h, gamma, beta, w_qkv, w_o, a, coords, cell_to_pos,
+                         gate, eps: float = 1e-5, workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h + PACK3D(projections of LayerNorm(h)) W_o^T, [N, C]."""
+    n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
+    width = h.shape[1]
+    gshape = (n, hq, 2) if prob.gate_per_head else (n, 2)
+    if workspace is None:
+        size = pack3d_layer_workspace_size(prob, width)
+        if size == 0:
+            _check(LIB.pack3d_layer_forward(ctypes.byref(prob), width, None, None, None, eps,
+                                            None, None, None, None, None, None, None, None, 0,
+                                            None))
+        workspace = torch.empty(size, dtype=torch.uint8, device=h.device)
+    out = _empty((n, width), dt, h) if out is None else out
+    _check(LIB.pack3d_layer_forward(
+        ctypes.byref(prob), width, _ptr(h, dt, (n, width), "h"),
+        _ptr(gamma, torch.float32, (width,), "gamma"), _ptr(beta, torch.float32, (width,), "beta"),
+        eps, _ptr(w_qkv, dt, ((hq + 4 * hkv) * 64, width), "w_qkv"),
+        _ptr(w_o, dt, (width, hq * 64), "w_o"), _ptr(a, torch.float32, (n, hkv), "a"),
+        _ptr(coords, torch.int32, (n, 3), "coords"),
+        _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"), _ptr(gate, torch.float32, gshape, "gate"),
+        _ptr(out, dt, (n, width), "out"), workspace.data_ptr(), workspace.numel(),
+        _stream(h.device)))
+    return out

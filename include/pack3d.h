@@ -258,6 +258,55 @@ int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc
 /* Bytes of workspace pack3d_backward needs for this problem (0 if invalid). */
 size_t pack3d_backward_workspace_size(const pack3d_problem* prob);
 
+/*
+ * The layer around the operator (notes, flowchart node B "linear projection
+ * and layer normalisation produce Q, K_loc, V_loc, K_cmp, V_cmp" and node G
+ * "residual output"; key design 1 writes q = R(c) W_Q LN(h),
+ * k^b = R(c) W_K^b LN(h), v^b = W_V^b LN(h)).  bf16 tensors only; the
+ * model width is `width` (a multiple of 64 in [64, 8192]).
+ *
+ * pack3d_layernorm_qkv: x = LayerNorm(h) over the width (biased variance,
+ * x = (h - mean) / sqrt(var + eps) * gamma + beta; gamma/beta fp32 [width]
+ * or NULL for 1/0), then the bias-free projections y = x W_qkv^T with
+ * W_qkv bf16 [Hq*64 + 4*Hkv*64, width] row-major, its rows stacked in the
+ * order Q, K_loc, V_loc, K_cmp, V_cmp.  Q and K_loc are rotated by R(c_i)
+ * before their single rounding: q_rot [N, Hq, 64], k_rot [N, Hkv, 64];
+ * v_loc, k_cmp, v_cmp [N, Hkv, 64] unrotated (k_cmp is rotated per cell
+ * inside the summaries).  q_raw (nullable) also receives the unrotated Q (the
+ * coordinate-blind compressed branch reads it).  h bf16 [N, width];
+ * ln_stats fp32 [N, 2] receives each token's mean and 1/sqrt(var + eps).
+ */
+int pack3d_layernorm_qkv(const pack3d_problem* prob, int32_t width, const void* h,
+                         const float* gamma, const float* beta, float eps, const void* w_qkv,
+                         const int32_t* coords, float* ln_stats, void* q_rot, void* q_raw,
+                         void* k_rot, void* v_loc, void* k_cmp, void* v_cmp, void* stream);
+
+/*
+ * Output projection with the residual (notes, flowchart node G):
+ *   out[i, :] = residual[i, :] + o[i, :] W_o^T
+ * o bf16 [N, Hq*64] (the heads' gated outputs, concatenated); W_o bf16
+ * [width, Hq*64]; residual, out bf16 [N, width] (out must not alias o).
+ */
+int pack3d_out_proj(const pack3d_problem* prob, int32_t width, const void* o, const void* w_o,
+                    const void* residual, void* out, void* stream);
+
+/*
+ * The whole layer: h' = h + PACK3D(LayerNorm(h) projections) W_o^T, i.e.
+ * pack3d_layernorm_qkv, the block summaries, local attention, the
+ * query->summary attention with the gate, and pack3d_out_proj, on one
+ * stream.  a, coords, cell_to_pos, gate_logits as in pack3d_forward;
+ * out bf16 [N, width] (must not alias h).  workspace: at least
+ * pack3d_layer_workspace_size() bytes, 256-byte aligned, caller-owned.
+ */
+int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* h,
+                         const float* gamma, const float* beta, float eps, const void* w_qkv,
+                         const void* w_o, const float* a, const int32_t* coords,
+                         const int32_t* cell_to_pos, const float* gate_logits, void* out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace pack3d_layer_forward needs (0 if invalid). */
+size_t pack3d_layer_workspace_size(const pack3d_problem* prob, int32_t width);
+
 /* Bytes of workspace pack3d_forward needs for this problem (0 if invalid). */
 size_t pack3d_forward_workspace_size(const pack3d_problem* prob);
 

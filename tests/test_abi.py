@@ -172,3 +172,42 @@ def test_training_buffer_sizes_match_layout(pk):
     bad = _prob(pk, head_dim=16)
     assert pk.pack3d_saved_size(bad) == 0
     assert pk.pack3d_backward_workspace_size(bad) == 0
+
+
+def test_layer_entry_points_check_arguments_on_the_host(pk):
+    """fp32 tensors, a bad width, NULL tensors and a short workspace are
+    rejected before any launch."""
+    L = pk.LIB
+    p32 = _prob(pk, dtype=torch.float32)
+    pbf = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1)
+    f = ctypes.c_float(1e-5)
+    assert L.pack3d_out_proj(ctypes.byref(p32), 512, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert L.pack3d_out_proj(ctypes.byref(pbf), 100, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert "width" in pk.pack3d_last_error()
+    assert L.pack3d_out_proj(ctypes.byref(pbf), 512, None, FAKE, FAKE, FAKE, None) == -1
+    assert L.pack3d_layernorm_qkv(ctypes.byref(pbf), 512, FAKE, None, None, f, FAKE, FAKE, FAKE,
+                                  FAKE, None, FAKE, FAKE, FAKE, None, None) == -1
+    assert L.pack3d_layernorm_qkv(ctypes.byref(pbf), 512, FAKE, None, None, ctypes.c_float(0.0),
+                                  FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                  None) == -2
+    need = pk.pack3d_layer_workspace_size(pbf, 512)
+    assert need > 0 and pk.pack3d_layer_workspace_size(p32, 512) == 0
+    assert L.pack3d_layer_forward(ctypes.byref(pbf), 512, FAKE, None, None, f, FAKE, FAKE, None,
+                                  FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == -4
+    assert L.pack3d_layer_forward(ctypes.byref(pbf), 512, FAKE, None, None, f, FAKE, FAKE, None,
+                                  FAKE, FAKE, FAKE, FAKE, None, need, None) == -4
+
+
+def test_layer_workspace_layout(pk):
+    """Statistics, the five projections, summaries, o_loc, norms and the
+    gated output, each section 256-byte aligned (the unrotated Q only for
+    the coordinate-blind branch)."""
+    a256 = lambda b: (b + 255) // 256 * 256
+    p = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1)
+    n, m, hq, hkv = 1024, 64, 4, 1
+    want = (a256(8 * n) + 2 * a256(2 * n * hq * 64) + 4 * a256(2 * n * hkv * 64)
+            + 2 * a256(2 * hkv * m * 64) + a256(4 * n * hq * 64) + a256(4 * hkv * m)
+            + a256(4 * hkv))
+    assert pk.pack3d_layer_workspace_size(p, 512) == want
+    pb = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1, summary_mode="blind")
+    assert pk.pack3d_layer_workspace_size(pb, 512) == want + a256(2 * n * hq * 64)
