@@ -224,8 +224,8 @@ const char* pack3d_backend_info(void) {
          "MFMA 32x32x16 bf16 / 32x32x2 f32, online softmax, fused gate epilogue in forward); "
          "gate_mix=k_gate_mix; backward (bf16, Hq/Hkv in {4,8,16}): k_bwd_prep, k_loc_dq, "
          "k_glob_dq, k_unrotate, k_loc_dkv, k_glob_dkv, k_sum_bwd (MFMA 32x32x16 bf16); "
-         "layer (bf16): k_ln_stats, k_gemm<qkv> (LayerNorm on the operand load, RoPE in the "
-         "epilogue), k_gemm<residual> (MFMA 32x32x16 bf16, 128x128 tiles); "
+         "layer (bf16): k_layernorm, k_gemm<qkv> (RoPE in the epilogue), k_gemm<residual> "
+         "(MFMA 32x32x16 bf16, 128x128 tiles, LDS-staged coalesced epilogues); "
          "no fallbacks";
 }
 
@@ -561,11 +561,11 @@ int check_width(const Geom& g, int32_t width, const char* fn) {
 }
 
 struct LayerLayout {
-  size_t stats, q_raw, q_rot, k_rot, v_loc, k_cmp, v_cmp, k_sum, v_sum, o_loc, knorm, kmax, o,
+  size_t x, q_raw, q_rot, k_rot, v_loc, k_cmp, v_cmp, k_sum, v_sum, o_loc, knorm, kmax, o,
       total;
 };
 
-LayerLayout layer_layout(const Geom& g) {
+LayerLayout layer_layout(const Geom& g, int32_t width) {
   LayerLayout w;
   size_t off = 0;
   auto take = [&](size_t& at, size_t bytes) {
@@ -573,7 +573,7 @@ LayerLayout layer_layout(const Geom& g) {
     off += align256(bytes);
   };
   const size_t nq = (size_t)g.N * g.Hq * 64 * 2, nk = (size_t)g.N * g.Hkv * 64 * 2;
-  take(w.stats, (size_t)g.N * 2 * 4);
+  take(w.x, (size_t)g.N * width * 2);
   take(w.q_raw, g.summary_mode == PACK3D_SUMMARY_BLIND ? nq : 0);
   take(w.q_rot, nq);
   take(w.k_rot, nk);
@@ -596,21 +596,21 @@ extern "C" {
 
 int pack3d_layernorm_qkv(const pack3d_problem* prob, int32_t width, const void* h,
                          const float* gamma, const float* beta, float eps, const void* w_qkv,
-                         const int32_t* coords, float* ln_stats, void* q_rot, void* q_raw,
+                         const int32_t* coords, void* x_norm, void* q_rot, void* q_raw,
                          void* k_rot, void* v_loc, void* k_cmp, void* v_cmp, void* stream) {
   static const char* fn = "pack3d_layernorm_qkv";
   Geom g;
   int rc = make_geom(prob, &g);
   if (rc || (rc = check_width(g, width, fn))) return rc;
-  if (!h || !w_qkv || !coords || !ln_stats || !q_rot || !k_rot || !v_loc || !k_cmp || !v_cmp)
+  if (!h || !w_qkv || !coords || !x_norm || !q_rot || !k_rot || !v_loc || !k_cmp || !v_cmp)
     return fail(PACK3D_ERR_NULL, "%s: NULL tensor argument", fn);
   if (!(eps > 0.0f) || !isfinite(eps)) return fail(PACK3D_ERR_SHAPE, "%s: eps must be > 0", fn);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if ((e = launch_ln_stats(g, width, h, eps, ln_stats, s)) != hipSuccess)
-    return hip_status(e, "k_ln_stats");
-  return hip_status(launch_qkv_proj(g, width, h, ln_stats, gamma, beta, w_qkv, coords, q_rot,
-                                    q_raw, k_rot, v_loc, k_cmp, v_cmp, s),
+  if ((e = launch_layernorm(g, width, h, gamma, beta, eps, x_norm, s)) != hipSuccess)
+    return hip_status(e, "k_layernorm");
+  return hip_status(launch_qkv_proj(g, width, x_norm, w_qkv, coords, q_rot, q_raw, k_rot, v_loc,
+                                    k_cmp, v_cmp, s),
                     "k_gemm<qkv>");
 }
 
@@ -629,7 +629,7 @@ size_t pack3d_layer_workspace_size(const pack3d_problem* prob, int32_t width) {
   Geom g;
   if (make_geom(prob, &g) != PACK3D_OK || check_width(g, width, "pack3d_layer_workspace_size"))
     return 0;
-  return layer_layout(g).total;
+  return layer_layout(g, width).total;
 }
 
 int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* h,
@@ -646,22 +646,20 @@ int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* 
   if (!(eps > 0.0f) || !isfinite(eps)) return fail(PACK3D_ERR_SHAPE, "%s: eps must be > 0", fn);
   if (!local_supported(g))
     return fail(PACK3D_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d unsupported", fn, g.G);
-  const LayerLayout w = layer_layout(g);
+  const LayerLayout w = layer_layout(g, width);
   if ((rc = check_buffer(workspace, ws_bytes, w.total, fn, "workspace"))) return rc;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  float* stats = (float*)(ws + w.stats);
   const bool blind = g.summary_mode == PACK3D_SUMMARY_BLIND;
   void* q_raw = blind ? ws + w.q_raw : nullptr;
   float* knorm = (float*)(ws + w.knorm);
   float* kmax = (float*)(ws + w.kmax);
   float* o_loc = (float*)(ws + w.o_loc);
   hipError_t e;
-  if ((e = launch_ln_stats(g, width, h, eps, stats, s)) != hipSuccess)
-    return hip_status(e, "k_ln_stats");
-  if ((e = launch_qkv_proj(g, width, h, stats, gamma, beta, w_qkv, coords, ws + w.q_rot, q_raw,
-                           ws + w.k_rot, ws + w.v_loc, ws + w.k_cmp, ws + w.v_cmp, s)) !=
-      hipSuccess)
+  if ((e = launch_layernorm(g, width, h, gamma, beta, eps, ws + w.x, s)) != hipSuccess)
+    return hip_status(e, "k_layernorm");
+  if ((e = launch_qkv_proj(g, width, ws + w.x, w_qkv, coords, ws + w.q_rot, q_raw, ws + w.k_rot,
+                           ws + w.v_loc, ws + w.k_cmp, ws + w.v_cmp, s)) != hipSuccess)
     return hip_status(e, "k_gemm<qkv>");
   if ((e = launch_block_summary(g, ws + w.k_cmp, ws + w.v_cmp, a, cell_to_pos, ws + w.k_sum,
                                 ws + w.v_sum, g.scale * 1.4426950408889634f, knorm, s)) !=

@@ -100,14 +100,12 @@ struct BwdBuffers {
 bool backward_supported(const Geom& g);
 int64_t glob_dkv_splits(const Geom& g);
 hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s);
-// The layer around the operator (bf16): LayerNorm statistics [N, 2] (mean,
-// 1/sqrt(var + eps)); the stacked projection with LayerNorm applied to its
-// input and RoPE to Q and K_loc (q_raw: unrotated Q as well, nullable); the
-// output projection out = resid + o W_o^T.
-hipError_t launch_ln_stats(const Geom& g, int32_t width, const void* h, float eps, float* stats,
-                           hipStream_t s);
-hipError_t launch_qkv_proj(const Geom& g, int32_t width, const void* h, const float* stats,
-                           const float* gamma, const float* beta, const void* w_qkv,
+// The layer around the operator (bf16): x = LayerNorm(h) [N, width]; the
+// stacked projection of x with RoPE on Q and K_loc (q_raw: unrotated Q as
+// well, nullable); the output projection out = resid + o W_o^T.
+hipError_t launch_layernorm(const Geom& g, int32_t width, const void* h, const float* gamma,
+                            const float* beta, float eps, void* x, hipStream_t s);
+hipError_t launch_qkv_proj(const Geom& g, int32_t width, const void* x, const void* w_qkv,
                            const int32_t* coords, void* q, void* q_raw, void* k_loc,
                            void* v_loc, void* k_cmp, void* v_cmp, hipStream_t s);
 hipError_t launch_out_proj(const Geom& g, int32_t width, const void* o, const void* w_o,

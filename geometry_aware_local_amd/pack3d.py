@@ -430,20 +430,20 @@ def pack3d_layernorm_qkv(prob: Problem, h, gamma, beta, w_qkv, coords, eps: floa
                          with_q_raw: bool = False) -> dict:
     """LayerNorm(h) projected by the stacked weight ``w_qkv`` [Hq*64 + 4*Hkv*64,
     C]: returns q_rot, k_rot (rotated by R(c)), v_loc, k_cmp, v_cmp, the
-    LayerNorm statistics ln_stats [N, 2] and, with ``with_q_raw``, q_raw."""
+    normalised input x_norm [N, C] and, with ``with_q_raw``, q_raw."""
     n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
     width = h.shape[1]
     out = {"q_rot": _empty((n, hq, 64), dt, h), "k_rot": _empty((n, hkv, 64), dt, h)}
     for name in ("v_loc", "k_cmp", "v_cmp"):
         out[name] = _empty((n, hkv, 64), dt, h)
-    out["ln_stats"] = _empty((n, 2), torch.float32, h)
+    out["x_norm"] = _empty((n, width), dt, h)
     if with_q_raw:
         out["q_raw"] = _empty((n, hq, 64), dt, h)
     _check(LIB.pack3d_layernorm_qkv(
         ctypes.byref(prob), width, _ptr(h, dt, (n, width), "h"),
         _ptr(gamma, torch.float32, (width,), "gamma"), _ptr(beta, torch.float32, (width,), "beta"),
         eps, _ptr(w_qkv, dt, ((hq + 4 * hkv) * 64, width), "w_qkv"),
-        _ptr(coords, torch.int32, (n, 3), "coords"), out["ln_stats"].data_ptr(),
+        _ptr(coords, torch.int32, (n, 3), "coords"), out["x_norm"].data_ptr(),
         out["q_rot"].data_ptr(), out["q_raw"].data_ptr() if with_q_raw else None,
         out["k_rot"].data_ptr(), out["v_loc"].data_ptr(), out["k_cmp"].data_ptr(),
         out["v_cmp"].data_ptr(), _stream(h.device)))

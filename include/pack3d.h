@@ -274,11 +274,11 @@ size_t pack3d_backward_workspace_size(const pack3d_problem* prob);
  * v_loc, k_cmp, v_cmp [N, Hkv, 64] unrotated (k_cmp is rotated per cell
  * inside the summaries).  q_raw (nullable) also receives the unrotated Q (the
  * coordinate-blind compressed branch reads it).  h bf16 [N, width];
- * ln_stats fp32 [N, 2] receives each token's mean and 1/sqrt(var + eps).
+ * x_norm bf16 [N, width] receives LayerNorm(h) (the projections' input).
  */
 int pack3d_layernorm_qkv(const pack3d_problem* prob, int32_t width, const void* h,
                          const float* gamma, const float* beta, float eps, const void* w_qkv,
-                         const int32_t* coords, float* ln_stats, void* q_rot, void* q_raw,
+                         const int32_t* coords, void* x_norm, void* q_rot, void* q_raw,
                          void* k_rot, void* v_loc, void* k_cmp, void* v_cmp, void* stream);
 
 /*

@@ -199,13 +199,13 @@ def test_layer_entry_points_check_arguments_on_the_host(pk):
 
 
 def test_layer_workspace_layout(pk):
-    """Statistics, the five projections, summaries, o_loc, norms and the
+    """LayerNorm(h), the five projections, summaries, o_loc, norms and the
     gated output, each section 256-byte aligned (the unrotated Q only for
     the coordinate-blind branch)."""
     a256 = lambda b: (b + 255) // 256 * 256
     p = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1)
     n, m, hq, hkv = 1024, 64, 4, 1
-    want = (a256(8 * n) + 2 * a256(2 * n * hq * 64) + 4 * a256(2 * n * hkv * 64)
+    want = (a256(2 * n * 512) + 2 * a256(2 * n * hq * 64) + 4 * a256(2 * n * hkv * 64)
             + 2 * a256(2 * hkv * m * 64) + a256(4 * n * hq * 64) + a256(4 * hkv * m)
             + a256(4 * hkv))
     assert pk.pack3d_layer_workspace_size(p, 512) == want

@@ -6,7 +6,8 @@ test_oracle_layer_pins.py).
 Tolerances (bf16 tensors, fp32 accumulation): each projection output within
 1e-2 of its largest magnitude (LayerNorm's output and every product operand
 are bf16, relative rounding <= 2^-9 each, and the output is rounded once);
-LayerNorm statistics to 1e-5 relative (fp32 on bf16-exact inputs).  The
+the LayerNorm output itself to one bf16 rounding (fp32 arithmetic on
+bf16-exact inputs).  The
 whole layer: the output projection is scaled up by 16 (exact in bf16) so the
 attention part is of the same size as the residual, and the layer's update
 out - h is held to 2e-2 of its largest magnitude plus the output's own bf16
@@ -74,12 +75,9 @@ def test_layernorm_qkv(pk, w, width):
     torch.cuda.synchronize()
     x = orc.layer_norm(L.h, L.gamma, L.beta)
     q, kl, vl, kc, vc = orc.qkv_projection(x, L.w_qkv, w.n_q_heads, w.n_kv_heads)
-    h64 = L.h.astype(np.float64)
-    mu = h64.mean(axis=1)
-    rstd = 1.0 / np.sqrt(((h64 - mu[:, None]) ** 2).mean(axis=1) + 1e-5)
-    st = gu.host(g["ln_stats"])
-    assert np.abs(st[:, 0] - mu).max() <= 1e-5
-    assert np.abs(st[:, 1] / rstd - 1).max() <= 1e-5
+    # LayerNorm in fp32 on bf16-exact inputs, one bf16 rounding
+    xn = gu.host(g["x_norm"])
+    assert np.all(np.abs(xn - x) <= 2.0 ** -8 * np.abs(x) + 1e-5)
     refs = dict(q_rot=orc.rotate(q, inp.coords), k_rot=orc.rotate(kl, inp.coords), v_loc=vl,
                 k_cmp=kc, v_cmp=vc, q_raw=q)
     for name, ref in refs.items():
