@@ -223,6 +223,9 @@ def main() -> int:
                     help="for counter runs: a known-size copy probe, then 3 forwards")
     ap.add_argument("--profile-backward", action="store_true",
                     help="with --profile-only: 3 training forwards + backwards instead")
+    ap.add_argument("--profile-layer", action="store_true",
+                    help="with --profile-only: 3 whole layers (LayerNorm + projections, "
+                         "operator, output projection) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the operator's "
@@ -256,7 +259,15 @@ def main() -> int:
         y = torch.empty_like(x)
         for _ in range(3):
             torch.neg(x, out=y)           # copy probe: reads and writes 256 MiB
-        if args.profile_backward:
+        if args.profile_layer:
+            L = sg.make_layer_inputs(inp)
+            bf = torch.bfloat16
+            lh = torch.from_numpy(L.h).to(bf).cuda()
+            lg, lb = torch.from_numpy(L.gamma).cuda(), torch.from_numpy(L.beta).cuda()
+            lq, lo = torch.from_numpy(L.w_qkv).to(bf).cuda(), torch.from_numpy(L.w_o).to(bf).cuda()
+            for _ in range(3):
+                pk.pack3d_layer_forward(prob, lh, lg, lb, lq, lo, a, coords, c2p, gate)
+        elif args.profile_backward:
             dout = dev(sg.make_upstream_grad(inp), dt)
             saved, grads = None, None
             for _ in range(3):
