@@ -63,12 +63,13 @@ hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
 // instead; the coordinate-blind variant does not rotate.
 // ---------------------------------------------------------------------------
 constexpr int kSumWaves = 4;
-constexpr int kMaxPasses = kMaxBlockVol / 8;
 
 // The forward asks for the key summaries multiplied by kscale (the softmax
 // scale in log2 units, applied once before the single rounding) and for the
 // norm of every scaled key summary in knorm [Hkv, M].
-template <typename T>
+// P = passes of 8 cells (block volume <= 8 P), fixed at compile time so the
+// per-cell rotations of small blocks take few registers.
+template <typename T, int P>
 __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
     const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ a,
     const int32_t* __restrict__ c2p, T* __restrict__ ks, T* __restrict__ vs, Geom g,
@@ -79,24 +80,21 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
   const int slot = lane >> 3, chunk = lane & 7;
   const int nbx = g.X / g.bx, nby = g.Y / g.by;
   const int jx = (int)(j % nbx), jy = (int)((j / nbx) % nby), jz = (int)(j / ((int64_t)nbx * nby));
-  const int passes = (g.bvol + 7) >> 3;
   const float uniform = 1.0f / (float)g.bvol;
   const bool per_cell = g.summary_mode == PACK3D_SUMMARY_TOKEN;
 
   // positions and rotations of the lane's cells (one per pass)
-  int64_t pos[kMaxPasses];
-  float sn[kMaxPasses][4], cs[kMaxPasses][4];
+  int64_t pos[P];
+  float sn[P][4], cs[P][4];
 #pragma unroll
-  for (int p = 0; p < kMaxPasses; ++p) {
+  for (int p = 0; p < P; ++p) {
     pos[p] = -1;
-    if (p < passes) {
-      const int u = p * 8 + slot;
-      if (u < g.bvol) {
-        const int ux = u % g.bx, uy = (u / g.bx) % g.by, uz = u / (g.bx * g.by);
-        const int z = jz * g.bz + uz, y = jy * g.by + uy, x = jx * g.bx + ux;
-        pos[p] = c2p[((int64_t)z * g.Y + y) * g.X + x];
-        if (per_cell) chunk_sincos(g.rope, chunk, z, y, x, sn[p], cs[p]);
-      }
+    const int u = p * 8 + slot;
+    if (u < g.bvol) {
+      const int ux = u % g.bx, uy = (u / g.bx) % g.by, uz = u / (g.bx * g.by);
+      const int z = jz * g.bz + uz, y = jy * g.by + uy, x = jx * g.bx + ux;
+      pos[p] = c2p[((int64_t)z * g.Y + y) * g.X + x];
+      if (per_cell) chunk_sincos(g.rope, chunk, z, y, x, sn[p], cs[p]);
     }
   }
 
@@ -105,8 +103,8 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
 #pragma unroll
     for (int i = 0; i < 8; ++i) ak[i] = av[i] = 0.0f;
 #pragma unroll
-    for (int p = 0; p < kMaxPasses; ++p) {
-      if (p < passes && pos[p] >= 0) {
+    for (int p = 0; p < P; ++p) {
+      if (pos[p] >= 0) {
         const int64_t row = (pos[p] * g.Hkv + grp) * 64 + chunk * 8;
         float kv[8], vv[8];
         load8<T>(kc + row, kv);
@@ -152,19 +150,30 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
   }
 }
 
+template <typename T>
+static void launch_sum_t(const Geom& g, const void* k_cmp, const void* v_cmp, const float* a,
+                         const int32_t* c2p, void* k_sum, void* v_sum, float kscale,
+                         float* knorm, hipStream_t s) {
+  const dim3 grid((unsigned)((g.M + kSumWaves - 1) / kSumWaves));
+  const dim3 block(64 * kSumWaves);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, (const T*)k_cmp, (const T*)v_cmp, a, c2p,
+                       (T*)k_sum, (T*)v_sum, g, kscale, knorm);
+  };
+  static_assert(kMaxBlockVol <= 64, "block volume");
+  if (g.bvol <= 8) go(k_block_summary<T, 1>);
+  else if (g.bvol <= 16) go(k_block_summary<T, 2>);
+  else if (g.bvol <= 32) go(k_block_summary<T, 4>);
+  else go(k_block_summary<T, 8>);
+}
+
 hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_cmp,
                                 const float* a, const int32_t* c2p, void* k_sum, void* v_sum,
                                 float kscale, float* knorm, hipStream_t s) {
-  const dim3 grid((unsigned)((g.M + kSumWaves - 1) / kSumWaves));
-  const dim3 block(64 * kSumWaves);
   if (g.bf16)
-    hipLaunchKernelGGL(k_block_summary<bf16_t>, grid, block, 0, s, (const bf16_t*)k_cmp,
-                       (const bf16_t*)v_cmp, a, c2p, (bf16_t*)k_sum, (bf16_t*)v_sum, g, kscale,
-                       knorm);
+    launch_sum_t<bf16_t>(g, k_cmp, v_cmp, a, c2p, k_sum, v_sum, kscale, knorm, s);
   else
-    hipLaunchKernelGGL(k_block_summary<float>, grid, block, 0, s, (const float*)k_cmp,
-                       (const float*)v_cmp, a, c2p, (float*)k_sum, (float*)v_sum, g, kscale,
-                       knorm);
+    launch_sum_t<float>(g, k_cmp, v_cmp, a, c2p, k_sum, v_sum, kscale, knorm, s);
   return hipGetLastError();
 }
 
