@@ -364,13 +364,18 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
   // staging: thread = (row, 16-byte chunk); chunk-0 threads also move the
   // row's lse and D (rows past the slice get lse = +inf: p = 0)
   const int srow = tid >> 3, sch = tid & 7;
+  const int head = grp * A.grp + srow % A.grp;
   u32x4 sq, sd;
   float sl = 0.0f, sdd = 0.0f;
-  auto load = [&](int64_t t) {
+  // the row's packed position for a tile (-1 past the slice); fetched one
+  // tile ahead of the row data so the two loads do not chain
+  auto position = [&](int64_t t) -> int32_t {
     const int64_t cell = c0 + t * cpt + srow / A.grp;
-    const int head = grp * A.grp + srow % A.grp;
-    if (cell < c1) {
-      const int64_t r = (int64_t)A.c2p[cell] * A.hq + head;
+    return cell < c1 ? A.c2p[cell] : -1;
+  };
+  auto load = [&](int32_t pos) {
+    if (pos >= 0) {
+      const int64_t r = (int64_t)pos * A.hq + head;
       sq = ld16(A.q + r * 64 + sch * 8);
       sd = ld16(A.dco + r * 64 + sch * 8);
       if (sch == 0) {
@@ -383,7 +388,9 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
       sdd = 0.0f;
     }
   };
-  if (nt > 0) load(0);
+  int32_t pnext = -1;
+  if (nt > 0) load(position(0));
+  if (nt > 1) pnext = position(1);
   for (int64_t t = 0; t < nt; ++t) {
     const int b = (int)(t & 1);
     st16(q_l[b] + TL::chunk_off(srow, sch), sq);
@@ -393,7 +400,10 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
       dd_l[b][srow] = sdd;
     }
     __syncthreads();
-    if (t + 1 < nt) load(t + 1);
+    if (t + 1 < nt) {
+      load(pnext);
+      if (t + 2 < nt) pnext = position(t + 2);
+    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       bf16x8 qr[4], dr[4];
