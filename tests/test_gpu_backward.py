@@ -40,6 +40,11 @@ CASES = [
     _w("deep_window", (9, 12, 8), 8, 2, window=(7, 3, 5), packing="morton", seed=8),
     _w("window_1", (2, 8, 8), 4, 1, window=(1, 1, 1), packing="raster", seed=9),
     _w("window_3x3x5", (4, 8, 16), 4, 1, window=(3, 3, 5), block=(2, 2, 4), seed=10),
+    # degenerate lattices: one token (N = M = 1), one summary for the whole
+    # lattice (block volume 64), a single row of cells
+    _w("single_cell", (1, 1, 1), 4, 1, block=(1, 1, 1), seed=11),
+    _w("one_summary", (2, 4, 8), 8, 2, block=(2, 4, 8), seed=12),
+    _w("one_row", (1, 1, 24), 16, 1, block=(1, 1, 4), seed=13),
 ]
 
 

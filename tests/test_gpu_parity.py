@@ -228,6 +228,44 @@ def test_branches_with_peaked_queries(pk):
     assert gu.max_rel(gu.host(o_cmp)[rows], ro_cmp) <= gu.REL_TOL["bf16"]
 
 
+def test_forward_softmax_reference_paths(pk):
+    """The fused forward picks, per wave, the zero reference (every query's
+    logit bound <= 64 in log2 units), a fixed reference (bounds <= 80) or a
+    tracked running max.  Queries are scaled per group of 16 tokens (one
+    wave's rows) by 1, 8 and 12, and mixed within a group, so all three
+    paths and mixed waves run; the gate is forced to the compressed branch.
+    The oracle gets the operands as the kernel holds them: rotated queries
+    and summaries pre-scaled by tau*log2(e), each rounded to bf16 (computed
+    on the host from the oracle's own values), softmax in base 2."""
+    w = MORTON.with_(grid=(4, 16, 16))
+    _say("softmax reference paths", w.name)
+    inp = sg.make_inputs(w)
+    n = w.n_tokens
+    grp_scale = np.array([1.0, 8.0, 12.0, 0.0])
+    scale = grp_scale[(np.arange(n) // 16) % 4]
+    mixed = scale == 0.0
+    scale[mixed] = np.random.default_rng(3).choice([1.0, 8.0, 12.0], int(mixed.sum()))
+    inp.q = sg.round_to_bf16((inp.q * scale[:, None, None]).astype(np.float32))
+    inp.gate = np.tile(np.array([[-60.0, 60.0]], np.float32), (n, 1))
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    out = gu.host(pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"],
+                                    d["a"], d["coords"], d["cell_to_pos"], d["gate"]))
+    q_r = gu.round_like(orc.rotate(inp.q, inp.coords), w)
+    ks, vs = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block)
+    ks2 = gu.round_like(ks * (0.125 / np.log(2.0)), w)
+    ref, _ = orc.global_attention(q_r, ks2, gu.round_like(vs, w), np.log(2.0))
+    # the three paths are all taken: bounds per token (log2 units)
+    kmax = np.sqrt((ks2 ** 2).sum(-1)).max()
+    bound = np.sqrt((q_r ** 2).sum(-1)).max(-1) * kmax
+    assert (bound <= 60).any() and ((bound > 66) & (bound < 78)).sum() > 64 and (bound > 84).any()
+    err = np.abs(out - ref) / np.abs(ref).max()
+    for name, sel in (("zero", bound <= 60), ("fixed", (bound > 66) & (bound < 78)),
+                      ("tracked", bound > 82)):
+        _say(f"  {name}: {int(sel.sum())} tokens, max error {err[sel].max():.2e} of max |o_cmp|")
+    assert err.max() <= gu.REL_TOL["bf16"]
+
+
 def test_forward_262k_block_sampled(pk):
     _say("forward", BLOCK.name)
     inp = sg.make_inputs(BLOCK)
@@ -346,6 +384,33 @@ def test_unit_blocks_give_dense_attention(pk, dtype):
         ref[:, h] = (p / p.sum(1, keepdims=True)) @ inp.v_cmp[:, h // grp].astype(np.float64)
     assert gu.max_abs(o, ref) <= gu.ABS_TOL[dtype]
     assert gu.max_rel(o, ref) <= gu.REL_TOL[dtype]
+
+
+EDGE = [
+    _w("single_cell_f32", (1, 1, 1), 4, 1, "f32", block=(1, 1, 1)),
+    _w("single_cell_bf16", (1, 1, 1), 8, 2, "bf16", block=(1, 1, 1)),
+    _w("one_summary_f32", (2, 4, 8), 4, 2, "f32", block=(2, 4, 8)),
+    _w("one_summary_bf16", (2, 4, 8), 8, 2, "bf16", block=(2, 4, 8), packing="morton"),
+    _w("one_row_bf16", (1, 1, 24), 16, 1, "bf16", block=(1, 1, 4)),
+    _w("one_column_f32", (5, 1, 1), 2, 1, "f32", window=(5, 1, 1), block=(5, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=[e.name for e in EDGE])
+def test_forward_degenerate_lattices(pk, w):
+    """One token (N = M = 1), one summary for the whole lattice (M = 1, block
+    volume 64), a 1x1xX row and a Zx1x1 column."""
+    _say("forward degenerate", w.name)
+    inp = sg.make_inputs(w)
+    out, o_loc, o_cmp, ref = _check_forward(pk, w, inp, np.arange(w.n_tokens))
+    if w.n_blocks == 1:
+        # a single summary: every query's compressed branch is that value
+        # summary, whatever the logits
+        _, vs = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block)
+        grp = w.n_q_heads // w.n_kv_heads
+        want = np.repeat(vs[:, 0][None], w.n_tokens, 0).repeat(grp, axis=1)
+        tol = 1e-5 if w.dtype == "f32" else 2.0 ** -7
+        assert np.abs(gu.host(o_cmp) - want).max() <= tol * max(1.0, np.abs(want).max())
 
 
 def test_window_of_one_cell_returns_values(pk):
