@@ -16,6 +16,10 @@
 //               fp32 before the single rounding; E = kResidual writes
 //               residual + Y.  The output tile is staged through LDS so every
 //               global store moves whole 16-byte chunks of 128-byte rows.
+//               256 x 256 tiles (8 waves of 64 features x 128 tokens): each
+//               token tile is read once per 256 features and each weight
+//               tile once per 256 tokens, which is what bounds a contraction
+//               this short (K = the model width) on this part.
 //
 // Feature rows are the MFMA rows, so a lane's accumulators hold 4
 // consecutive features of one token: rotary pairs (2p, 2p+1) stay in the
@@ -28,11 +32,24 @@ namespace ly {
 
 typedef KLds<bf16_t> TL;            // 64-element rows, bank-swizzled chunks
 
-constexpr int kT = 128;             // tokens per workgroup tile
-constexpr int kF = 128;             // features per workgroup tile
 constexpr int kK = 64;              // contraction step (one LDS row)
-constexpr int kWaves = 4;           // 2 x 2 waves, 64 x 64 outputs each
-constexpr int kStage = kT * 8 / (64 * kWaves);   // 16-byte chunks per thread per operand
+
+// Tile shape: WF x WT waves, each 64 features x 32*NJ tokens; the workgroup
+// covers 64*WF features x 32*NJ*WT tokens.
+template <int WF, int WT, int NJ>
+struct GTile {
+  static constexpr int W = WF * WT;
+  static constexpr int F = 64 * WF, T = 32 * NJ * WT;
+  static constexpr int SW = F * 8 / (64 * W), SX = T * 8 / (64 * W);   // chunks per thread
+  static_assert(F * 8 % (64 * W) == 0 && T * 8 % (64 * W) == 0, "whole chunks per thread");
+};
+// Both projections use 256 features x 256 tokens (8 waves).  Against 128 x
+// 128 tiles this halves the operand re-reads from L2 (the bound of a
+// contraction as short as the model width); the layer measured 0.67 -> 0.58
+// ms for LayerNorm + the stacked projection and 0.29 -> 0.25 ms for the
+// output projection at 262,144 tokens, width 512.
+typedef GTile<4, 2, 4> QkvTile;
+typedef GTile<4, 2, 4> OutTile;
 
 enum Epi { kQkv = 0, kResidual = 1 };
 
@@ -74,8 +91,9 @@ __device__ __forceinline__ void pair_sincos(const double* nu, const int* axis, i
   cs = ax < 0 ? 1.0f : cs;
 }
 
-template <int E>
-__global__ __launch_bounds__(64 * kWaves) void k_gemm(GemmArgs A) {
+template <int E, class Tile>
+__global__ __launch_bounds__(64 * Tile::W) void k_gemm(GemmArgs A) {
+  constexpr int W = Tile::W, kF = Tile::F, kT = Tile::T, NJ = kT / 32 / (W / (kF / 64));
   // operand tiles (double-buffered); after the contraction the same memory
   // stages the output tile for coalesced stores
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (kF + kT) * kK];
@@ -94,38 +112,42 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemm(GemmArgs A) {
   const int64_t t0 = tt * kT;
   const int f0 = ft * kF;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int fw = (wave & 1) * 64, tw = (wave >> 1) * 64;
+  const int fw = (wave % (kF / 64)) * 64, tw = (wave / (kF / 64)) * (32 * NJ);
   if (E == kQkv && tid < kMaxPairs) {        // read after the first barrier below
     const bool on = tid < A.rope.npairs;
     nu_l[tid] = on ? A.rope.nu[tid] : 0.0;
     ax_l[tid] = on ? A.rope.axis[tid] : -1;
   }
 
-  // staging: thread = (row tid/8 + 32 i, 16-byte chunk tid % 8)
+  // staging: thread = (row tid/8 + 8W i, 16-byte chunk tid % 8)
   const int sch = tid & 7;
-  u32x4 sw[kStage], sx[kStage];
+  u32x4 sw[Tile::SW], sx[Tile::SX];
   auto load = [&](int kk) {
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int fr = f0 + r;
-      const int64_t tr = t0 + r;
+    for (int i = 0; i < Tile::SW; ++i) {
+      const int fr = f0 + (tid >> 3) + 8 * W * i;
       sw[i] = fr < A.f_rows ? ld16(A.w + (int64_t)fr * A.k + kk + sch * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < Tile::SX; ++i) {
+      const int64_t tr = t0 + (tid >> 3) + 8 * W * i;
       sx[i] = tr < A.t_rows ? ld16(A.x + tr * A.k + kk + sch * 8) : u32x4{0, 0, 0, 0};
     }
   };
   auto store = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      st16(w_l(b) + TL::chunk_off(r, sch), sw[i]);
-      st16(x_l(b) + TL::chunk_off(r, sch), sx[i]);
-    }
+    for (int i = 0; i < Tile::SW; ++i)
+      st16(w_l(b) + TL::chunk_off((tid >> 3) + 8 * W * i, sch), sw[i]);
+#pragma unroll
+    for (int i = 0; i < Tile::SX; ++i)
+      st16(x_l(b) + TL::chunk_off((tid >> 3) + 8 * W * i, sch), sx[i]);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
   const int nk = A.k / kK;
   load(0);
   for (int ks = 0; ks < nk; ++ks) {
@@ -133,60 +155,65 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemm(GemmArgs A) {
     store(b);
     __syncthreads();
     if (ks + 1 < nk) load((ks + 1) * kK);
-    bf16x8 af[2][4], xf[2][4];
+    bf16x8 af[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) row_frags(w_l(b), fw + 32 * i + col, h, af[i]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) row_frags(x_l(b), tw + 32 * j + col, h, xf[j]);
+    for (int j = 0; j < NJ; ++j) {
+      bf16x8 xf[4];
+      row_frags(x_l(b), tw + 32 * j + col, h, xf);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = Mma<bf16_t>::mma(af[i][s], xf[j][s], acc[i][j]);
+        for (int i = 0; i < 2; ++i) acc[i][j] = Mma<bf16_t>::mma(af[i][s], xf[s], acc[i][j]);
+    }
   }
   __syncthreads();                  // operand tiles free: reuse for the output
 
   // Accumulator layout: lane = token tw + 32 j + col, element 4 q4 + e =
   // feature fw + 32 i + 8 q4 + 4 h + e of the tile.
+  // The output is staged in rounds; round r holds token blocks JR r ..
+  // JR r + JR - 1 of every wave, so all waves work in every round.  Staged
+  // row sr is token t0 + (sr / (32 JR)) (32 NJ) + 32 JR r + sr % (32 JR).
+  constexpr int kWT = W / (kF / 64);
   if (E == kResidual) {
-    // fp32 staging in two halves of 64 tokens: [64][kOS32] floats
+    constexpr int JR = 1, RR = kWT * 32 * JR;      // rows per round
     constexpr int kOS32 = kF + 4;
+    static_assert(NJ % JR == 0 && RR * kF / 8 % (64 * W) == 0, "whole rounds");
+    static_assert(RR * kOS32 * 4 <= (int)sizeof(lds), "staging fits the operand tiles");
     float* ot = reinterpret_cast<float*>(lds);
+#pragma unroll 1
+    for (int r = 0; r < NJ / JR; ++r) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (tw == 64 * half) {
+      for (int j = 0; j < NJ; ++j) {
+        if (j / JR != r) continue;
+        const int sr = (tw / (32 * NJ)) * 32 * JR + (j % JR) * 32 + col;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 v;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              f32x4 v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q4 + e];
-              *reinterpret_cast<f32x4*>(ot + (32 * j + col) * kOS32 + fw + 32 * i + 8 * q4 +
-                                        4 * h) = v;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q4 + e];
+            *reinterpret_cast<f32x4*>(ot + sr * kOS32 + fw + 32 * i + 8 * q4 + 4 * h) = v;
+          }
       }
       __syncthreads();
-      // 64 tokens x 16 chunks of 8 features; 4 chunks per thread
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int c = tid + 256 * c4, tl = c >> 4, fc = (c & 15) * 8;
-        const int64_t t = t0 + 64 * half + tl;
+      for (int c8 = 0; c8 < RR * kF / 8 / (64 * W); ++c8) {
+        const int c = tid + 64 * W * c8, sr = c / (kF / 8), fc = (c % (kF / 8)) * 8;
+        const int64_t t = t0 + (sr / (32 * JR)) * 32 * NJ + 32 * JR * r + sr % (32 * JR);
         const int f = f0 + fc;
         if (t < A.t_rows && f < A.f_rows) {
-          const f32x4 a0 = *reinterpret_cast<const f32x4*>(ot + tl * kOS32 + fc);
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(ot + tl * kOS32 + fc + 4);
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(ot + sr * kOS32 + fc);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(ot + sr * kOS32 + fc + 4);
           const int64_t o = t * A.f_rows + f;
-          const bf16x8 r = *reinterpret_cast<const bf16x8*>(A.resid + o);
+          const bf16x8 rs = *reinterpret_cast<const bf16x8*>(A.resid + o);
           bf16x8 out;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            out[e] = (bf16_t)((float)r[e] + a0[e]);
-            out[4 + e] = (bf16_t)((float)r[4 + e] + a1[e]);
+            out[e] = (bf16_t)((float)rs[e] + a0[e]);
+            out[4 + e] = (bf16_t)((float)rs[4 + e] + a1[e]);
           }
           *reinterpret_cast<bf16x8*>(A.y + o) = out;
         }
@@ -194,80 +221,80 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemm(GemmArgs A) {
       __syncthreads();
     }
   } else {
-    // bf16 staging of the whole tile: [128 tokens][kOS16], then 16-byte
-    // stores of each (token, projection head) 128-byte row.  With q_raw the
-    // unrotated Q tile is staged and stored first.
+    // bf16 staging in rounds of 128 tokens: [128][kOS16], then 16-byte stores
+    // of each (token, projection head) 128-byte row.  With q_raw the
+    // unrotated Q is staged and stored first.
+    constexpr int JR = 2, RR = kWT * 32 * JR;      // rows per round
     constexpr int kOS16 = kF + 8;
+    static_assert(NJ % JR == 0 && RR * kF / 8 % (64 * W) == 0, "whole rounds");
+    static_assert(RR * kOS16 * 2 <= (int)sizeof(lds), "staging fits the operand tiles");
     bf16_t* ot = lds;
-    int cz[2], cy[2], cx[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t t = t0 + tw + 32 * j + col;
-      cz[j] = cy[j] = cx[j] = 0;
-      if (t < A.t_rows) {
-        cz[j] = A.coords[3 * t];
-        cy[j] = A.coords[3 * t + 1];
-        cx[j] = A.coords[3 * t + 2];
-      }
-    }
+    const int seg = (f0 + fw) >> 6;               // the wave's 64 features: one head
+    const bool rotatable = (seg < A.hq || (seg - A.hq) / A.hkv == 0) && seg < A.hq + 4 * A.hkv;
     const bool raw_pass = A.q_raw != nullptr && f0 < A.hq * 64;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll 1
+    for (int pass = raw_pass ? 0 : 1; pass < 2; ++pass) {
       const bool rotate = pass == 1;
-      if (!rotate && !raw_pass) continue;
+#pragma unroll 1
+      for (int r = 0; r < NJ / JR; ++r) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int seg = (f0 + fw) >> 6;         // the wave's 64 features: one head
-          const bool rot = rotate && (seg < A.hq || (seg - A.hq) / A.hkv == 0) &&
-                           seg < A.hq + 4 * A.hkv;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q4 + e];
-            if (rot) {
-              // dims 32 i + 8 q4 + 4 h .. +3: pairs p and p + 1
-              const int p = 16 * i + 4 * q4 + 2 * h;
-#pragma unroll
-              for (int pp = 0; pp < 2; ++pp) {
-                float sn, cs;
-                pair_sincos(nu_l, ax_l, p + pp, cz[j], cy[j], cx[j], sn, cs);
-                const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
-                v[2 * pp] = cs * x0 - sn * x1;
-                v[2 * pp + 1] = sn * x0 + cs * x1;
-              }
-            }
-            bf16x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16_t)v[e];
-            *reinterpret_cast<bf16x4*>(ot + (tw + 32 * j + col) * kOS16 + fw + 32 * i + 8 * q4 +
-                                       4 * h) = o;
+        for (int j = 0; j < NJ; ++j) {
+          if (j / JR != r) continue;
+          const int sr = (tw / (32 * NJ)) * 32 * JR + (j % JR) * 32 + col;
+          const int64_t t = t0 + tw + 32 * j + col;
+          int cz = 0, cy = 0, cx = 0;
+          if (rotate && rotatable && t < A.t_rows) {
+            cz = A.coords[3 * t];
+            cy = A.coords[3 * t + 1];
+            cx = A.coords[3 * t + 2];
           }
-        }
-      __syncthreads();
-      // 128 tokens x 16 chunks of 8 features; 8 chunks per thread
 #pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) {
-        const int c = tid + 256 * c8, tl = c >> 4, fc = (c & 15) * 8;
-        const int64_t t = t0 + tl;
-        const int f = f0 + fc;
-        if (t >= A.t_rows || f >= A.f_rows) continue;
-        const int seg = f >> 6, dim = f & 63;
-        bf16_t* dst;
-        int heads, head;
-        if (seg < A.hq) {
-          dst = rotate ? A.q : A.q_raw, heads = A.hq, head = seg;
-        } else {
-          if (!rotate) continue;
-          const int s2 = seg - A.hq, part = s2 / A.hkv;
-          heads = A.hkv, head = s2 % A.hkv;
-          dst = part == 0 ? A.k_loc : part == 1 ? A.v_loc : part == 2 ? A.k_cmp : A.v_cmp;
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q4 + e];
+              if (rotate && rotatable) {
+                // dims 32 i + 8 q4 + 4 h .. +3: pairs p and p + 1
+                const int p = 16 * i + 4 * q4 + 2 * h;
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                  float sn, cs;
+                  pair_sincos(nu_l, ax_l, p + pp, cz, cy, cx, sn, cs);
+                  const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
+                  v[2 * pp] = cs * x0 - sn * x1;
+                  v[2 * pp + 1] = sn * x0 + cs * x1;
+                }
+              }
+              bf16x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = (bf16_t)v[e];
+              *reinterpret_cast<bf16x4*>(ot + sr * kOS16 + fw + 32 * i + 8 * q4 + 4 * h) = o;
+            }
         }
-        st16(dst + (t * heads + head) * 64 + dim, ld16(ot + tl * kOS16 + fc));
+        __syncthreads();
+#pragma unroll
+        for (int c8 = 0; c8 < RR * kF / 8 / (64 * W); ++c8) {
+          const int c = tid + 64 * W * c8, sr = c / (kF / 8), fc = (c % (kF / 8)) * 8;
+          const int64_t t = t0 + (sr / (32 * JR)) * 32 * NJ + 32 * JR * r + sr % (32 * JR);
+          const int f = f0 + fc;
+          if (t >= A.t_rows || f >= A.f_rows) continue;
+          const int sg = f >> 6, dim = f & 63;
+          bf16_t* dst;
+          int heads, head;
+          if (sg < A.hq) {
+            dst = rotate ? A.q : A.q_raw, heads = A.hq, head = sg;
+          } else {
+            if (!rotate) continue;
+            const int s2 = sg - A.hq, part = s2 / A.hkv;
+            heads = A.hkv, head = s2 % A.hkv;
+            dst = part == 0 ? A.k_loc : part == 1 ? A.v_loc : part == 2 ? A.k_cmp : A.v_cmp;
+          }
+          st16(dst + (t * heads + head) * 64 + dim, ld16(ot + sr * kOS16 + fc));
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
 }
@@ -360,13 +387,14 @@ hipError_t launch_layernorm(const Geom& g, int32_t width, const void* h, const f
   return hipGetLastError();
 }
 
+template <class Tile>
 static void gemm_grid(ly::GemmArgs& A, int64_t t_rows, int32_t f_rows, int32_t k) {
   A.t_rows = t_rows;
   A.f_rows = f_rows;
   A.k = k;
-  const int64_t tiles = (t_rows + ly::kT - 1) / ly::kT;
+  const int64_t tiles = (t_rows + Tile::T - 1) / Tile::T;
   A.nt = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
-  A.nf = (f_rows + ly::kF - 1) / ly::kF;
+  A.nf = (f_rows + Tile::F - 1) / Tile::F;
 }
 
 hipError_t launch_qkv_proj(const Geom& g, int32_t width, const void* x, const void* w_qkv,
@@ -375,7 +403,8 @@ hipError_t launch_qkv_proj(const Geom& g, int32_t width, const void* x, const vo
   ly::GemmArgs A = {};
   A.w = (const bf16_t*)w_qkv;
   A.x = (const bf16_t*)x;
-  gemm_grid(A, g.N, (g.Hq + 4 * g.Hkv) * 64, width);
+  typedef ly::QkvTile Tile;
+  gemm_grid<Tile>(A, g.N, (g.Hq + 4 * g.Hkv) * 64, width);
   A.q = (bf16_t*)q;
   A.q_raw = (bf16_t*)q_raw;
   A.k_loc = (bf16_t*)k_loc;
@@ -386,7 +415,7 @@ hipError_t launch_qkv_proj(const Geom& g, int32_t width, const void* x, const vo
   A.hkv = g.Hkv;
   A.coords = coords;
   A.rope = g.rope;
-  hipLaunchKernelGGL(ly::k_gemm<ly::kQkv>, dim3((unsigned)(A.nt * A.nf)), dim3(64 * ly::kWaves),
+  hipLaunchKernelGGL((ly::k_gemm<ly::kQkv, Tile>), dim3((unsigned)(A.nt * A.nf)), dim3(64 * Tile::W),
                      0, s, A);
   return hipGetLastError();
 }
@@ -396,11 +425,12 @@ hipError_t launch_out_proj(const Geom& g, int32_t width, const void* o, const vo
   ly::GemmArgs A = {};
   A.w = (const bf16_t*)w_o;
   A.x = (const bf16_t*)o;
-  gemm_grid(A, g.N, width, g.Hq * 64);
+  typedef ly::OutTile Tile;
+  gemm_grid<Tile>(A, g.N, width, g.Hq * 64);
   A.resid = (const bf16_t*)resid;
   A.y = (bf16_t*)out;
-  hipLaunchKernelGGL(ly::k_gemm<ly::kResidual>, dim3((unsigned)(A.nt * A.nf)),
-                     dim3(64 * ly::kWaves), 0, s, A);
+  hipLaunchKernelGGL((ly::k_gemm<ly::kResidual, Tile>), dim3((unsigned)(A.nt * A.nf)),
+                     dim3(64 * Tile::W), 0, s, A);
   return hipGetLastError();
 }
 

@@ -225,7 +225,7 @@ const char* pack3d_backend_info(void) {
          "gate_mix=k_gate_mix; backward (bf16, Hq/Hkv in {4,8,16}): k_bwd_prep, k_loc_dq, "
          "k_glob_dq, k_unrotate, k_loc_dkv, k_glob_dkv, k_sum_bwd (MFMA 32x32x16 bf16); "
          "layer (bf16): k_layernorm, k_gemm<qkv> (RoPE in the epilogue), k_gemm<residual> "
-         "(MFMA 32x32x16 bf16, 128x128 tiles, LDS-staged coalesced epilogues); "
+         "(MFMA 32x32x16 bf16, 256x256 tiles of 8 waves, LDS-staged coalesced epilogues); "
          "no fallbacks";
 }
 
