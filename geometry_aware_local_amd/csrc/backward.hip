@@ -361,49 +361,47 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
   const int64_t c1 = c0 + A.cps < A.ncell ? c0 + A.cps : A.ncell;
   const int cpt = kKRows / A.grp;                    // cells per tile
   const int64_t nt = c1 > c0 ? (c1 - c0 + cpt - 1) / cpt : 0;
-  // staging: thread = (row, 16-byte chunk); chunk-0 threads also move the
-  // row's lse and D (rows past the slice get lse = +inf: p = 0)
+  // staging: thread = (row, 16-byte chunk); chunk-0 threads also store the
+  // row's lse and D (rows past the slice get lse = +inf: p = 0).  Two tiles
+  // are in flight in registers: a tile's rows are loaded two tiles before
+  // they are stored to LDS, and their packed positions one tile before that.
   const int srow = tid >> 3, sch = tid & 7;
   const int head = grp * A.grp + srow % A.grp;
-  u32x4 sq, sd;
-  float sl = 0.0f, sdd = 0.0f;
-  // the row's packed position for a tile (-1 past the slice); fetched one
-  // tile ahead of the row data so the two loads do not chain
-  auto position = [&](int64_t t) -> int32_t {
+  struct Stage {
+    u32x4 q, d;
+    float l, dd;
+    bool ok;
+  };
+  Stage sg0, sg1;
+  // every step issues the same loads (clamped addresses, results selected
+  // afterwards), so the memory-counter waits stay exact across the loop
+  // A position is the raw table entry plus a validity flag computed from the
+  // cell index alone, so nothing waits for the entry until the rows are due.
+  struct Pos {
+    int32_t p;
+    bool ok;
+  };
+  auto position = [&](int64_t t) -> Pos {
     const int64_t cell = c0 + t * cpt + srow / A.grp;
-    return cell < c1 ? A.c2p[cell] : -1;
+    return Pos{A.c2p[cell < c1 ? cell : c1 - 1], cell < c1};
   };
-  auto load = [&](int32_t pos) {
-    if (pos >= 0) {
-      const int64_t r = (int64_t)pos * A.hq + head;
-      sq = ld16(A.q + r * 64 + sch * 8);
-      sd = ld16(A.dco + r * 64 + sch * 8);
-      if (sch == 0) {
-        sl = A.lse[r] * kLog2e;
-        sdd = A.dd[r];
-      }
-    } else {
-      sq = sd = u32x4{0u, 0u, 0u, 0u};
-      sl = __builtin_inff();
-      sdd = 0.0f;
-    }
+  auto load = [&](Stage& sg, Pos pos) {
+    sg.ok = pos.ok;
+    const int64_t r = (int64_t)(pos.ok ? pos.p : 0) * A.hq + head;
+    sg.q = ld16(A.q + r * 64 + sch * 8);
+    sg.d = ld16(A.dco + r * 64 + sch * 8);
+    sg.l = A.lse[r];
+    sg.dd = A.dd[r];
   };
-  int32_t pnext = -1;
-  if (nt > 0) load(position(0));
-  if (nt > 1) pnext = position(1);
-  for (int64_t t = 0; t < nt; ++t) {
-    const int b = (int)(t & 1);
-    st16(q_l[b] + TL::chunk_off(srow, sch), sq);
-    st16(d_l[b] + TL::chunk_off(srow, sch), sd);
-    if (sch == 0) {
-      ls_l[b][srow] = sl;
-      dd_l[b][srow] = sdd;
-    }
-    __syncthreads();
-    if (t + 1 < nt) {
-      load(pnext);
-      if (t + 2 < nt) pnext = position(t + 2);
-    }
+  auto store = [&](const Stage& sg, int b) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    st16(q_l[b] + TL::chunk_off(srow, sch), sg.ok ? sg.q : z);
+    st16(d_l[b] + TL::chunk_off(srow, sch), sg.ok ? sg.d : z);
+    // the row's 8 threads write the same values
+    ls_l[b][srow] = sg.ok ? sg.l * kLog2e : __builtin_inff();
+    dd_l[b][srow] = sg.ok ? sg.dd : 0.0f;
+  };
+  auto tile = [&](int b) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       bf16x8 qr[4], dr[4];
@@ -441,6 +439,39 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
           dk[db] = Mma<bf16_t>::mma(qt[tt], dsf[tt], dk[db]);
         }
       }
+    }
+  };
+  // One step: publish tile t (held in sg), then refill sg with tile t + 2.
+  // Positions run one tile ahead of the rows and are issued before them, so
+  // waiting for a position never waits for the rows loaded after it.  The
+  // stream is padded to an even number of tiles (a padding tile has no rows:
+  // p = 0, adding exact zeros).
+  Pos pnext;
+  auto step = [&](Stage& sg, int64_t t) {
+    const int b = (int)(t & 1);
+    store(sg, b);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const Pos pn = position(t + 3);
+    load(sg, pnext);
+    pnext = pn;
+    __builtin_amdgcn_sched_barrier(0);
+    tile(b);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (nt > 0) {
+    // the same issue order as a step: position, then the rows
+    const Pos p0 = position(0), p1 = position(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(sg0, p0);
+    __builtin_amdgcn_sched_barrier(0);
+    pnext = position(2);
+    __builtin_amdgcn_sched_barrier(0);
+    load(sg1, p1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t t = 0; t < nt; t += 2) {
+      step(sg0, t);
+      step(sg1, t + 1);
     }
   }
   if (!kok) return;
