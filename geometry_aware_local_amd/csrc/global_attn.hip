@@ -11,8 +11,10 @@
 //   row being a (token, head) pair of that group: the G heads sharing the
 //   group's summaries are stacked as MFMA columns, so every summary tile
 //   staged in LDS feeds all of them.
-// * Summary tiles of 64 keys are double-buffered in LDS as plain row-major
-//   copies (16-byte chunks XOR-swizzled against bank conflicts).  Each wave
+// * Summary tiles of 64 keys live in LDS as plain row-major copies (16-byte
+//   chunks XOR-swizzled against bank conflicts).  bf16: phases of 4 tiles,
+//   copied global -> LDS asynchronously one phase ahead, one barrier per
+//   phase; fp32: register-staged double buffering.  Each wave
 //   computes S^T = K Q^T and O^T += V^T P^T with 32x32 MFMA tiles (see
 //   pack3d_device.h); the V^T operand comes straight from the row-major tile
 //   through the gfx950 transposing LDS read (ds_read_b64_tr_b16).
@@ -27,6 +29,7 @@
 // * Workgroups are ordered so that all the workgroups an XCD receives read
 //   the same KV group, keeping one group's summaries resident in its L2.
 #include "pack3d_device.h"
+#include "local_tiles.h"
 
 namespace pack3d {
 
@@ -166,7 +169,8 @@ struct GCol {
 
 // One 64-key tile for all of the wave's column blocks.
 template <typename T, int CB, int MODE>
-__device__ __forceinline__ void g_tile(const T* kl, const T* vl, int64_t k0, int64_t m,
+__device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __restrict__ vl,
+                                       int64_t k0, int64_t m,
                                        float c, const QFrag<T> (&qf)[CB], GCol (&st)[CB],
                                        f32x16 (&o)[CB][2], int lane) {
   const int h = lane >> 5, col = lane & 31;
@@ -261,12 +265,77 @@ __device__ __forceinline__ void g_stream(T (&k_lds)[2][kGKt * 64],
   }
 }
 
+// bf16 stream: phases of kPhR tiles.  The tiles of the next phase are copied
+// global -> LDS asynchronously (one 1 KB copy of 8 key rows per wave and
+// operand) while the waves work through the current phase with no barrier
+// between its tiles; one barrier per phase publishes the copies and frees
+// the previous phase's buffers.  Keys past M read the last summary (finite)
+// and are masked to p = 0.  Two separate LDS arrays hold the two phases so
+// the compiler can tell the copies in flight from the tiles being read.
+constexpr int kPhR = 4;                      // tiles per phase
+constexpr int kPhTile = 2 * kGKt * 64;       // K then V, elements
+
+template <int I>
+__device__ __forceinline__ bf16_t* ph_buf() {
+  __shared__ __attribute__((aligned(16))) bf16_t buf[kPhR * kPhTile];
+  return buf;
+}
+
+__device__ __forceinline__ void g_issue_ph(bf16_t* __restrict__ buf, int64_t ph, const bf16_t* ksg,
+                                           const bf16_t* vsg, int64_t m, int64_t nt, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int row = wave * 8 + (lane >> 3), pos = lane & 7;
+  const int ksw = pos ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  const int vsw = pos ^ ((2 * row) & 6);
+#pragma unroll
+  for (int i = 0; i < kPhR; ++i) {
+    const int64_t t = ph * kPhR + i;
+    if (t < nt) {
+      const int64_t key = t * kGKt + row;
+      const int64_t kc = key < m ? key : m - 1;
+      bf16_t* dst = buf + i * kPhTile + wave * 512;
+      __builtin_amdgcn_global_load_lds((const void*)(ksg + kc * 64 + ksw * 8), (lb::lds_ptr)dst, 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds((const void*)(vsg + kc * 64 + vsw * 8),
+                                       (lb::lds_ptr)(dst + kGKt * 64), 16, 0, 0);
+    }
+  }
+}
+
+template <int CB, int MODE>
+__device__ __forceinline__ void g_stream_ph(const bf16_t* ksg, const bf16_t* vsg,
+                                            const GArgs<bf16_t>& A,
+                                            const QFrag<bf16_t> (&qf)[CB], GCol (&st)[CB],
+                                            f32x16 (&o)[CB][2], int tid, int lane) {
+  const int64_t nt = (A.m + kGKt - 1) / kGKt;
+  const int64_t nph = (nt + kPhR - 1) / kPhR;
+  auto phase = [&](int64_t ph, bf16_t* __restrict__ cur, bf16_t* __restrict__ nxt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (ph + 1 < nph) g_issue_ph(nxt, ph + 1, ksg, vsg, A.m, nt, tid);
+#pragma unroll
+    for (int i = 0; i < kPhR; ++i) {
+      const int64_t t = ph * kPhR + i;
+      if (t < nt)
+        g_tile<bf16_t, CB, MODE>(cur + i * kPhTile, cur + i * kPhTile + kGKt * 64, t * kGKt, A.m,
+                                 A.c, qf, st, o, lane);
+    }
+  };
+  for (int64_t ph = 0; ph < nph; ph += 2) {
+    phase(ph, ph_buf<0>(), ph_buf<1>());
+    if (ph + 1 < nph) phase(ph + 1, ph_buf<1>(), ph_buf<0>());
+  }
+}
+
 template <typename T, bool kGate>
 __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   constexpr int CB = GCfg<T>::kCb;
   constexpr int ROWS = kGWaves * CB * 32;
-  __shared__ __attribute__((aligned(16))) T k_lds[2][kGKt * 64];
-  __shared__ __attribute__((aligned(16))) T v_lds[2][GLds<T>::kVElems];
+  constexpr bool kAsync = !GLds<T>::kF32;
+  typedef T KTile[2][kGKt * 64];
+  typedef T VTile[2][GLds<T>::kVElems];
+  __shared__ __attribute__((aligned(16))) KTile k_lds_f32;
+  __shared__ __attribute__((aligned(16))) VTile v_lds_f32;
 
   // workgroup -> (KV group, query tile), XCD-aware
   const int64_t bid = blockIdx.x;
@@ -288,7 +357,10 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   const T* vsg = A.vs + (int64_t)grp * A.m * 64;
 
   GStage<T> stage;
-  g_load<T>(stage, ksg, vsg, 0, A.m, tid);
+  if constexpr (kAsync)
+    g_issue_ph(ph_buf<0>(), 0, ksg, vsg, A.m, (A.m + kGKt - 1) / kGKt, tid);
+  else
+    g_load<T>(stage, ksg, vsg, 0, A.m, tid);
 
   // query fragments of this lane's columns, and their softmax references
   QFrag<T> qf[CB];
@@ -337,12 +409,21 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   }
 
   // one code path per wave; each query's arithmetic is the same in all of them
-  if (A.kmax && __all(all_zero))
-    g_stream<T, CB, kZeroRef>(k_lds, v_lds, stage, ksg, vsg, A, qf, st, o, tid, lane);
-  else if (A.kmax && __all(all_fixed))
-    g_stream<T, CB, kFixedRef>(k_lds, v_lds, stage, ksg, vsg, A, qf, st, o, tid, lane);
-  else
-    g_stream<T, CB, kGeneral>(k_lds, v_lds, stage, ksg, vsg, A, qf, st, o, tid, lane);
+  if constexpr (kAsync) {
+    if (A.kmax && __all(all_zero))
+      g_stream_ph<CB, kZeroRef>(ksg, vsg, A, qf, st, o, tid, lane);
+    else if (A.kmax && __all(all_fixed))
+      g_stream_ph<CB, kFixedRef>(ksg, vsg, A, qf, st, o, tid, lane);
+    else
+      g_stream_ph<CB, kGeneral>(ksg, vsg, A, qf, st, o, tid, lane);
+  } else {
+    if (A.kmax && __all(all_zero))
+      g_stream<T, CB, kZeroRef>(k_lds_f32, v_lds_f32, stage, ksg, vsg, A, qf, st, o, tid, lane);
+    else if (A.kmax && __all(all_fixed))
+      g_stream<T, CB, kFixedRef>(k_lds_f32, v_lds_f32, stage, ksg, vsg, A, qf, st, o, tid, lane);
+    else
+      g_stream<T, CB, kGeneral>(k_lds_f32, v_lds_f32, stage, ksg, vsg, A, qf, st, o, tid, lane);
+  }
 
   // epilogue: normalise, write o_cmp or the gated output
 #pragma unroll
