@@ -81,7 +81,7 @@ def _gpu(pk, w, inp, dout, gate):
 
 def _rel(got, ref):
     # a gradient that is exactly zero (e.g. dk_loc with a 1x1x1 window:
-    # softmax over one key has no key gradient) is judged on a 1e-2 scale
+    # softmax over one key has no key gradient) is held to a 1e-2 scale
     return gu.max_abs(got, ref) / max(float(np.abs(ref).max()), 1e-2)
 
 
