@@ -228,26 +228,47 @@ __global__ __launch_bounds__(64 * Tile::W) void k_gemm(GemmArgs A) {
     constexpr int kOS16 = kF + 8;
     static_assert(NJ % JR == 0 && RR * kF / 8 % (64 * W) == 0, "whole rounds");
     static_assert(RR * kOS16 * 2 <= (int)sizeof(lds), "staging fits the operand tiles");
+    // The round's rotary table follows the staging area: row sr holds (sin,
+    // cos) of every pair for the token of staged row sr, computed once per
+    // workgroup instead of once per head (rows padded by 16 bytes so the 32
+    // lanes of a half-wave read different banks).
+    constexpr int kTabS = 2 * 32 + 4;
+    static_assert(RR * kOS16 * 2 + RR * kTabS * 4 <= (int)sizeof(lds), "table fits");
+    static_assert(RR * 4 == 64 * W, "one table task per thread");
     bf16_t* ot = lds;
+    float* tab = reinterpret_cast<float*>(lds + RR * kOS16);
     const int seg = (f0 + fw) >> 6;               // the wave's 64 features: one head
     const bool rotatable = (seg < A.hq || (seg - A.hq) / A.hkv == 0) && seg < A.hq + 4 * A.hkv;
+    const bool any_rot = f0 < (A.hq + A.hkv) * 64;  // the tile holds a Q or K_loc head
     const bool raw_pass = A.q_raw != nullptr && f0 < A.hq * 64;
 #pragma unroll 1
     for (int pass = raw_pass ? 0 : 1; pass < 2; ++pass) {
       const bool rotate = pass == 1;
 #pragma unroll 1
       for (int r = 0; r < NJ / JR; ++r) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          if (j / JR != r) continue;
-          const int sr = (tw / (32 * NJ)) * 32 * JR + (j % JR) * 32 + col;
-          const int64_t t = t0 + tw + 32 * j + col;
+        if (rotate && any_rot) {
+          // task: staged row tid / 4, pairs 8 (tid % 4) .. + 7
+          const int sr = tid >> 2, pg = tid & 3;
+          const int64_t t = t0 + (sr / (32 * JR)) * 32 * NJ + 32 * JR * r + sr % (32 * JR);
           int cz = 0, cy = 0, cx = 0;
-          if (rotate && rotatable && t < A.t_rows) {
+          if (t < A.t_rows) {
             cz = A.coords[3 * t];
             cy = A.coords[3 * t + 1];
             cx = A.coords[3 * t + 2];
           }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float s0, c0, s1, c1;
+            pair_sincos(nu_l, ax_l, 8 * pg + 2 * u, cz, cy, cx, s0, c0);
+            pair_sincos(nu_l, ax_l, 8 * pg + 2 * u + 1, cz, cy, cx, s1, c1);
+            *reinterpret_cast<f32x4*>(tab + sr * kTabS + 16 * pg + 4 * u) = f32x4{s0, c0, s1, c1};
+          }
+          __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (j / JR != r) continue;
+          const int sr = (tw / (32 * NJ)) * 32 * JR + (j % JR) * 32 + col;
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -258,10 +279,10 @@ __global__ __launch_bounds__(64 * Tile::W) void k_gemm(GemmArgs A) {
               if (rotate && rotatable) {
                 // dims 32 i + 8 q4 + 4 h .. +3: pairs p and p + 1
                 const int p = 16 * i + 4 * q4 + 2 * h;
+                const f32x4 w = *reinterpret_cast<const f32x4*>(tab + sr * kTabS + 2 * p);
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp) {
-                  float sn, cs;
-                  pair_sincos(nu_l, ax_l, p + pp, cz, cy, cx, sn, cs);
+                  const float sn = w[2 * pp], cs = w[2 * pp + 1];
                   const float x0 = v[2 * pp], x1 = v[2 * pp + 1];
                   v[2 * pp] = cs * x0 - sn * x1;
                   v[2 * pp + 1] = sn * x0 + cs * x1;
