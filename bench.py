@@ -313,7 +313,8 @@ def main() -> int:
     gbs = lambda b, t: b / (t * 1e-3) / 1e9
     tfl = lambda f, t: f / (t * 1e-3) / 1e12
     # kernel serving each stage (see pack3d_backend_info)
-    local_kernel = ("k_local_bf16" if w.dtype == "bf16" and w.n_q_heads // w.n_kv_heads in (4, 8, 16)
+    fast_local = w.dtype == "bf16" and w.n_q_heads // w.n_kv_heads in (4, 8, 16)
+    local_kernel = (("k_local_zrun" if w.window[0] == 3 else "k_local_bf16") if fast_local
                     else "k_local_attn")
     kernels = {
         "k_rope(q)": {"ms": stages["rope(q)"], "bound": "hbm",

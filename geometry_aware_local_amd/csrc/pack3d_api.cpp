@@ -218,9 +218,12 @@ const char* pack3d_last_error(void) { return g_err.c_str(); }
 const char* pack3d_backend_info(void) {
   return "libpack3d gfx950: rope=k_rope (VALU, 16B rows); "
          "block_summary=k_block_summary (wave per block, XOR-tree reduction); "
-         "local_attn=k_local_bf16 for bf16 with Hq/Hkv in {4,8,16} (async double-buffered "
-         "LDS planes, transposing V reads, masked-dense MFMA 32x32x16 bf16), else k_local_attn "
-         "(LDS plane tiles + halo, masked-dense MFMA 32x32x16 bf16 / 32x32x2 f32); global_attn=k_global_attn (summary tiles in LDS: bf16 copied asynchronously in phases of 4 tiles, fp32 register-staged double buffers; "
+         "local_attn for bf16 with Hq/Hkv in {4,8,16}: k_local_zrun for windows of 3 planes "
+         "(runs of query planes, 3-slot LDS ring of K/V planes), else k_local_bf16 (async "
+         "double-buffered LDS planes); both transposing V reads, masked-dense MFMA 32x32x16 "
+         "bf16; else k_local_attn (LDS plane tiles + halo, masked-dense MFMA 32x32x16 bf16 / "
+         "32x32x2 f32); global_attn=k_global_attn (summary tiles in LDS: bf16 copied "
+         "asynchronously in phases of 4 tiles, fp32 register-staged double buffers; "
          "MFMA 32x32x16 bf16 / 32x32x2 f32, online softmax, fused gate epilogue in forward); "
          "gate_mix=k_gate_mix; backward (bf16, Hq/Hkv in {4,8,16}): k_bwd_prep, k_loc_dq, "
          "k_glob_dq, k_unrotate, k_loc_dkv, k_glob_dkv, k_sum_bwd (MFMA 32x32x16 bf16); "
