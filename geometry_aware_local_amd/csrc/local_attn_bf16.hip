@@ -271,7 +271,6 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
   }
 }
 
-
 // ---------------------------------------------------------------------------
 // k_local_zrun: the tile, patches, masks and per-plane arithmetic of
 // k_local_bf16, for windows of three planes (z radius 1).  A
@@ -454,7 +453,7 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
     }
   };
 
-  auto finish = [&](int z0, int32_t qpos) __attribute__((always_inline)) {
+  auto finish = [&](int32_t qpos) __attribute__((always_inline)) {
     const float l = pair_sum(sm.l);
     if (qok) {
       const float inv = 1.0f / l;
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
     if (z0 + 3 < A.Z && z0 + 2 < ze) load_pos(z0 + 3, pos_n);
     compute_plane(qf, kb_, vb);
     if (z0 + 1 < A.Z) compute_plane(qf, kc, vc);
-    finish(z0, qpos);
+    finish(qpos);
     qf = qf_n;
     qpos = qpos_n;
     qpos_n = qpos_nn;
