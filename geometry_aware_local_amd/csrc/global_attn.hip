@@ -451,6 +451,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = o[cb][db][4 * q4 + j] * inv;
         if constexpr (kGate) {
+          if (A.o_cmp) *reinterpret_cast<f32x4*>(A.o_cmp + rbase + d0) = r;
           const f32x4 ol = *reinterpret_cast<const f32x4*>(A.o_loc + rbase + d0);
           if constexpr (GLds<T>::kF32) {
             f32x4 w;
@@ -531,7 +532,9 @@ hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_su
                               const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
                               float* lse, const float* o_loc, const float* gate, void* out,
                               hipStream_t s) {
-  const bool gated = o_cmp == nullptr;
+  // gated: the epilogue mixes with the local branch and writes O (and o_cmp
+  // too when given, for the backward)
+  const bool gated = out != nullptr;
   // with kmax the summaries carry the softmax scale in log2 units already
   const float c = kmax ? 1.0f : g.scale * kLog2e;
   if (g.bf16)

@@ -475,10 +475,10 @@ int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* 
   if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, lse_loc, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
   const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? q : q_rot;
-  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, nullptr, nullptr,
-                         nullptr, s);
-  if (e != hipSuccess) return hip_status(e, "k_global_attn");
-  return hip_status(launch_gate_mix(g, o_loc, o_cmp, gate_logits, out, s), "k_gate_mix");
+  // the compressed branch with the gate fused, also saving o_cmp and lse_cmp
+  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, o_loc, gate_logits,
+                         out, s);
+  return hip_status(e, "k_global_attn");
 }
 
 int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc,

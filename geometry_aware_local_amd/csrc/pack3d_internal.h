@@ -57,8 +57,9 @@ bool local_bf16_serves(int G);
 hipError_t launch_local_attn_bf16(const Geom& g, const void* q_rot, const void* k_rot,
                                   const void* v, const int32_t* cell_to_pos, float* o_loc,
                                   float* lse, hipStream_t s);
-// o_cmp != nullptr: write o_cmp (fp32).  Otherwise gate-mix epilogue:
-// out = g_loc*o_loc + g_cmp*o_cmp in the problem dtype.  kmax != nullptr:
+// out != nullptr: gate-mix epilogue, out = g_loc*o_loc + g_cmp*o_cmp in the
+// problem dtype (o_cmp, fp32, also written when non-null).  Otherwise o_cmp
+// (fp32) only.  lse != nullptr: natural-log lse per row.  kmax != nullptr:
 // the key summaries are pre-scaled by scale*log2(e) and kmax[g] bounds their
 // norms (enables the fixed softmax reference); nullptr: unscaled summaries.
 hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
