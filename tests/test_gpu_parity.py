@@ -47,6 +47,12 @@ SMALL = [
     _w("g16_bf16_full", (3, 4, 12), 16, 1, "bf16", packing="morton"),
     _w("g4_bf16_deep", (9, 12, 8), 8, 2, "bf16", window=(7, 3, 5), packing="morton"),
     _w("g4_bf16_w1", (2, 8, 8), 4, 1, "bf16", window=(1, 1, 1), packing="raster"),
+    # windows three planes deep on deeper lattices: the local kernel walks
+    # runs of query planes (runs of 4 here, the last one ragged, runs that
+    # start inside the lattice) for every heads-per-group ratio
+    _w("zrun_bf16_g4", (13, 8, 16), 8, 2, "bf16", window=(3, 5, 7)),
+    _w("zrun_bf16_g8", (10, 12, 8), 8, 1, "bf16", window=(3, 7, 3), packing="morton"),
+    _w("zrun_bf16_g16", (7, 4, 8), 16, 1, "bf16"),
 ]
 IDS = [w.name for w in SMALL]
 
