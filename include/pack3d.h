@@ -220,7 +220,8 @@ int pack3d_forward_timed(const pack3d_problem* prob, const void* q, const void* 
  * log-sum-exp of each branch's scaled logits), in that order, each section
  * starting on a 256-byte boundary.  saved: device memory of at least
  * pack3d_saved_size() bytes, 256-byte aligned, caller-owned.  The gate is
- * applied by a separate pass over the saved branch outputs.  Errors as
+ * applied in the compressed branch's epilogue, as in pack3d_forward, so out
+ * is bit for bit the same as pack3d_forward's.  Errors as
  * pack3d_forward (PACK3D_ERR_WORKSPACE also for `saved`).
  */
 int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* k_loc,

@@ -157,6 +157,23 @@ def test_backward_deterministic(pk):
         assert torch.equal(g1[n], g2[n]), n
 
 
+@pytest.mark.parametrize("w", [C5_SMALL, CASES[1], CASES[3], CASES[5]], ids=lambda w: w.name)
+def test_training_forward_output_is_the_forward_bitwise(pk, w):
+    """The training forward mixes the gate in the same epilogue as the
+    inference forward, so both give the same O bit for bit; its saved o_cmp
+    and lse are those of the compressed branch (checked against the oracle
+    through the backward tests)."""
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    args = (prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"], d["coords"],
+            d["cell_to_pos"], d["gate"])
+    out_train, _ = pk.pack3d_forward_train(*args)
+    out = pk.pack3d_forward(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out_train, out)
+
+
 def test_backward_262k_sampled(pk):
     """The backward workload at full size: dq and dgate on sampled tokens,
     dk_loc / dv_loc on sampled keys (their whole windows computed by the
