@@ -1,4 +1,5 @@
-"""Python binding of libpack3d: the PACK3D local-global attention forward on MI355X.
+"""Python binding of libpack3d: the PACK3D local-global attention operator on MI355X
+(forward, training forward and backward, and the layer around it).
 
 Argument marshalling only.  Every step of the operator runs in libpack3d's
 HIP kernels; PyTorch provides device memory and the current HIP stream.  The
