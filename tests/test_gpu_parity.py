@@ -53,6 +53,7 @@ SMALL = [
     _w("zrun_bf16_g4", (13, 8, 16), 8, 2, "bf16", window=(3, 5, 7)),
     _w("zrun_bf16_g8", (10, 12, 8), 8, 1, "bf16", window=(3, 7, 3), packing="morton"),
     _w("zrun_bf16_g16", (7, 4, 8), 16, 1, "bf16"),
+    _w("zrun_bf16_z2", (2, 8, 8), 8, 2, "bf16", packing="raster"),
 ]
 IDS = [w.name for w in SMALL]
 
