@@ -174,7 +174,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const bf16_t* __restrict__ dou
 // ---------------------------------------------------------------------------
 // k_glob_dq: workgroup = 8 waves = one KV group x 512 query rows (two
 // 32-column blocks per wave), summaries streamed in 64-key tiles double-
-// buffered in LDS through registers.
+// buffered in LDS through registers (the next tile's loads are issued after
+// the barrier and land while the current tile is computed).
 // ---------------------------------------------------------------------------
 constexpr int kGW = 8, kGCb = 2, kGRows = kGW * kGCb * 32, kGKt = 64;
 
@@ -236,14 +237,16 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
 
   // one 16-byte chunk of K and of V per thread per tile
   const int srow = tid >> 3, sch = tid & 7;
+  // Tile base pointers are uniform and lane offsets 32-bit, so no 64-bit
+  // address stays live across the loop.  Keys past M read the last summary
+  // (finite); their p is masked to 0.
   auto load = [&](int64_t t, u32x4& sk, u32x4& sv) {
-    const int64_t key = t * kGKt + srow;
-    if (key < A.m) {
-      sk = ld16(ksg + key * 64 + sch * 8);
-      sv = ld16(vsg + key * 64 + sch * 8);
-    } else {
-      sk = sv = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int64_t k0 = t * kGKt;
+    const int64_t left = A.m - 1 - k0;
+    const int lim = left < kGKt - 1 ? (int)left : kGKt - 1;
+    const uint32_t off = (uint32_t)(srow < lim ? srow : lim) * 128u + (uint32_t)sch * 16u;
+    sk = ld16(reinterpret_cast<const bf16_t*>(reinterpret_cast<const char*>(ksg + k0 * 64) + off));
+    sv = ld16(reinterpret_cast<const bf16_t*>(reinterpret_cast<const char*>(vsg + k0 * 64) + off));
   };
   u32x4 sk, sv;
   load(0, sk, sv);
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
           for (int v = 0; v < 16; ++v)
             ds[v] = __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -lse2[cb])) * (dp[v] - ddv[cb]);
         } else {
-          // keys past M: zero rows in LDS, p = 0
+          // keys past M: p = 0
           const int lim = (int)(A.m - t * kGKt) - kb * 32 - 4 * h;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
