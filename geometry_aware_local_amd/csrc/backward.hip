@@ -239,7 +239,7 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
   const int srow = tid >> 3, sch = tid & 7;
   // Tile base pointers are uniform and lane offsets 32-bit, so no 64-bit
   // address stays live across the loop.  Keys past M read the last summary
-  // (finite); their p is masked to 0.
+  // (finite; M >= 1 since the block divides the grid); their p is masked to 0.
   auto load = [&](int64_t t, u32x4& sk, u32x4& sv) {
     const int64_t k0 = t * kGKt;
     const int64_t left = A.m - 1 - k0;
