@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 METRIC = "PACK3D attention fwd tokens/sec at 262k tokens; % bf16 MFMA peak; HBM GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_global_attn_block_bf16_64x64x64_hbm_traffic.txt")
 GLOBAL_SOURCES = [os.path.join(ROOT, "geometry_aware_local_amd", "csrc", f)
-                  for f in ("global_attn.hip", "pack3d_device.h")]
+                  for f in ("global_attn.hip", "pack3d_device.h")] + [
+                  os.path.join(ROOT, "geometry_aware_local_amd", "build.py")]
 
 
 def source_sha(paths) -> str:
