@@ -10,10 +10,14 @@ on a bounded sample of the same workload on this host's cores.  A second leg
 ("training") times the training forward plus the backward (all six input
 gradients) on the same inputs with a seeded upstream gradient, and a third
 ("layer") the layer around the operator: LayerNorm + the five projections
-with RoPE, the operator, the output projection + residual (width Hq*64).
+with RoPE, the operator, the output projection + residual (width Hq*64), and
+a fourth ("c4_1m_random") the 1 048 576-token random-packing forward beside
+dense axial-RoPE attention on the same inputs.  The step time is the median
+over the timed steps; a plain 1 GiB device copy reports the achievable HBM
+bandwidth beside the 8 TB/s peak.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--dense]
-                    [--no-backward] [--no-layer] [--summary-mode MODE]
+                    [--no-backward] [--no-layer] [--no-c4] [--summary-mode MODE]
 """
 
 from __future__ import annotations
@@ -63,12 +67,21 @@ def measured_traffic():
     return float(val.group(1))
 
 
+def window_pairs(grid, window) -> int:
+    """Sum over all cells of the clipped box window's size.  The clipped box
+    is a product of per-axis intervals, so the sum factors over the axes."""
+    total = 1
+    for n, wa in zip(grid, window):
+        r = wa // 2
+        total *= sum(min(c + r, n - 1) - max(c - r, 0) + 1 for c in range(n))
+    return total
+
+
 def algorithmic(w: sg.Workload) -> dict:
     """Work each step must do, per kernel (what the method moves or computes)."""
-    import oracle.pack3d_oracle as orc  # window counts only (closed form)
     n, hq, hkv, m = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.n_blocks
     es = 2 if w.dtype == "bf16" else 4
-    nbr = int(orc.local_window_sizes(sg.lattice_cells(w.grid), w.grid, w.window).sum())
+    nbr = window_pairs(w.grid, w.window)
     return {
         # rope: read + write Q and K_loc, read coords (twice: one launch each)
         "rope_bytes": 2 * n * (hq + hkv) * 64 * es + 2 * n * 12,
@@ -92,8 +105,11 @@ def cpu_baseline(w: sg.Workload, inp: sg.Inputs, rows: int) -> dict:
     time is extrapolated linearly in the number of query tokens."""
     import threadpoolctl
     from oracle import pack3d_oracle as orc
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
+    blas = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    threads = min(cores, blas)
     sel = np.sort(np.random.default_rng(0).choice(w.n_tokens, rows, replace=False))
+    limiter = threadpoolctl.threadpool_limits(limits=threads)
     t0 = time.perf_counter()
     k_rot = orc.rotate(inp.k_loc, inp.coords, w.rope_pairs, w.rope_base)
     ks, vs = orc.block_summaries(inp.k_cmp, inp.v_cmp, inp.a, inp.coords, w.grid, w.block,
@@ -105,12 +121,100 @@ def cpu_baseline(w: sg.Workload, inp: sg.Inputs, rows: int) -> dict:
     oc, _ = orc.global_attention(q_rot, ks, vs, 0.125, q_is_rows=True)
     orc.gate_mix(ol, oc, inp.gate[sel])
     t2 = time.perf_counter()
+    limiter.restore_original_limits()
     whole = (t1 - t0) + (t2 - t1) * w.n_tokens / rows
     return {"value": w.n_tokens / whole, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "affinity_cores": cores, "cpu_model": cpu_model(),
+            "threads_note": "BLAS threads (the oracle's only parallel part), capped at the "
+                            "process's CPU affinity",
             "sample": f"{rows} of {w.n_tokens} query tokens (all heads), rotated keys and "
                       f"summaries in full; {t2 - t0:.1f} s measured, whole job extrapolated "
                       f"linearly in query tokens to {whole:.0f} s"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_probe(torch) -> dict:
+    """Achievable HBM bandwidth on this GPU: a plain device copy of 1 GiB
+    (read + write), median of 10 timed copies."""
+    x = torch.empty(256 << 20, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        y.copy_(x)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del x, y
+    gbs = 2 * (1 << 30) / (ms * 1e-3) / 1e9
+    return {"bytes": 2 * (1 << 30), "ms": ms, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
+def c4_leg(pk, torch, steps) -> dict:
+    """The 1 048 576-token workload (random packing, M = 65 536): the forward,
+    and dense axial-RoPE attention on the same inputs (1x1x1 blocks, a = 1,
+    m = N), for the speedup of PACK3D over dense attention."""
+    w = sg.WORKLOADS["random_bf16_64x128x128"]
+    print(f"[bench] C4 leg: {w.name}, generating inputs", file=sys.stderr, flush=True)
+    inp = sg.make_inputs(w)
+    bf = torch.bfloat16
+    dev = lambda x, t=None: None if x is None else (torch.from_numpy(x).to(t) if t else
+                                                    torch.from_numpy(x)).cuda()
+    q, k_loc, v_loc = dev(inp.q, bf), dev(inp.k_loc, bf), dev(inp.v_loc, bf)
+    k_cmp, v_cmp = dev(inp.k_cmp, bf), dev(inp.v_cmp, bf)
+    a, coords, c2p, gate = dev(inp.a), dev(inp.coords), dev(inp.cell_to_pos), dev(inp.gate)
+    del inp
+    prob = pk.make_problem(w.grid, w.n_q_heads, w.n_kv_heads, w.window, w.block, bf,
+                           w.rope_pairs, w.rope_base)
+    fargs = (prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, c2p, gate)
+    ws = pk.alloc_workspace(prob, q.device)
+    out = torch.empty_like(q)
+    pk.pack3d_forward(*fargs, workspace=ws, out=out)
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pk.pack3d_forward(*fargs, workspace=ws, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    f_ms = float(np.median(ts))
+    del ws, out
+    dprob = pk.make_problem(w.grid, w.n_q_heads, w.n_kv_heads, w.window, (1, 1, 1), bf,
+                            w.rope_pairs, w.rope_base)
+    q_rot = pk.pack3d_rope(prob, q, coords)
+    dk, dv = pk.pack3d_block_summary(dprob, k_cmp, v_cmp, None, c2p)
+    pk.pack3d_global_attn(dprob, q_rot, dk, dv)          # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    pk.pack3d_global_attn(dprob, q_rot, dk, dv)
+    e1.record()
+    torch.cuda.synchronize()
+    d_ms = e0.elapsed_time(e1)
+    n = w.n_tokens
+    g_flops = 4 * n * w.n_q_heads * w.n_blocks * 64
+    d_flops = 4 * n * w.n_q_heads * n * 64
+    print(f"[bench] C4: forward {f_ms:.2f} ms, dense {d_ms:.1f} ms, speedup {d_ms / f_ms:.1f}x",
+          file=sys.stderr, flush=True)
+    return {"workload": w.name, "tokens": n, "forward_ms": f_ms, "forward_steps": steps,
+            "tokens_per_s": n / (f_ms * 1e-3),
+            "compressed_branch_tflop": g_flops / 1e12,
+            "dense_ms": d_ms, "dense_tflops": d_flops / (d_ms * 1e-3) / 1e12,
+            "speedup_pack3d_vs_dense": d_ms / f_ms}
 
 
 def training_leg(pk, torch, w, inp, dev, dt, fargs, ws, out, args, work, peak_mfma) -> dict:
@@ -218,6 +322,8 @@ def main() -> int:
                     help="skip the training leg (forward_train + backward)")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the layer leg (LayerNorm + projections, operator, output proj)")
+    ap.add_argument("--no-c4", action="store_true",
+                    help="skip the 1M-token leg (forward + dense axial-RoPE companion)")
     ap.add_argument("--summary-mode", default="token", choices=("token", "centre", "blind"),
                     help="compressed-branch variant (token: the exact rotate-before-sum form)")
     ap.add_argument("--profile-only", action="store_true",
@@ -297,11 +403,16 @@ def main() -> int:
         pk.pack3d_forward_timed(*fargs, evs, workspace=ws, out=out)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = events[0][0].elapsed_time(events[-1][-1]) / args.steps
-    stage_ms = [sum(evs[i].elapsed_time(evs[i + 1]) for evs in events) / args.steps
+    # per step: first event to last event of that step; the step time is the
+    # median over the timed steps, each stage's time too
+    step_ms = [evs[0].elapsed_time(evs[-1]) for evs in events]
+    ms = float(np.median(step_ms))
+    mean_ms = events[0][0].elapsed_time(events[-1][-1]) / args.steps
+    stage_ms = [float(np.median([evs[i].elapsed_time(evs[i + 1]) for evs in events]))
                 for i in range(nev - 1)]
     stages = dict(zip(pk.FORWARD_STAGE_NAMES, stage_ms))
-    print(f"[bench] forward {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); " +
+    print(f"[bench] forward {ms:.3f} ms/step median (mean {mean_ms:.3f}, wall "
+          f"{1e3 * wall / args.steps:.3f}); " +
           ", ".join(f"{k} {v:.3f}" for k, v in stages.items()), file=sys.stderr, flush=True)
 
     work = algorithmic(w)
@@ -357,6 +468,9 @@ def main() -> int:
             "ms": dms, "tflops": tfl(dfl, dms), "frac": tfl(dfl, dms) / peak_mfma,
             "speedup_pack3d_vs_dense": dms / ms}
 
+    hbm = copy_probe(torch)
+    print(f"[bench] copy probe: {hbm['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+
     training = None
     if not args.no_backward and w.dtype == "bf16":   # the backward takes bf16
         training = training_leg(pk, torch, w, inp, dev, dt, fargs, ws, out, args, work, peak_mfma)
@@ -364,6 +478,10 @@ def main() -> int:
     layer = None
     if not args.no_layer and w.dtype == "bf16":     # the layer takes bf16
         layer = layer_leg(pk, torch, w, inp, fargs, args, peak_mfma)
+
+    c4 = None
+    if not args.no_c4 and w.name == "block_bf16_64x64x64":
+        c4 = c4_leg(pk, torch, max(args.steps // 4, 2))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -378,6 +496,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_mean": mean_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -392,8 +511,10 @@ def main() -> int:
                      "frac": g_tflops / peak_mfma, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "hbm_copy_probe": hbm,
         "training": training,
         "layer": layer,
+        "c4_1m_random": c4,
         **extra,
     }
     print(json.dumps(line), flush=True)

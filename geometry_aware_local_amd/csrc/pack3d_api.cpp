@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <string>
 
 #include "pack3d_internal.h"
@@ -199,6 +200,32 @@ BwdLayout bwd_layout(const Geom& g) {
   return w;
 }
 
+// Every device array must start on a 16-byte boundary: the kernels move rows
+// with 16-byte vector loads and stores and 16-byte direct-to-LDS copies.
+// Host check only (the pointer value), before any launch.
+struct Arr {
+  const void* p;
+  const char* name;
+};
+
+int check_aligned(const char* fn, std::initializer_list<Arr> arrs) {
+  for (const Arr& a : arrs)
+    if (a.p && ((uintptr_t)a.p & 15))
+      return fail(PACK3D_ERR_SHAPE, "%s: %s is not 16-byte aligned", fn, a.name);
+  return PACK3D_OK;
+}
+
+// The operator's inputs and output, as the forward entry points take them.
+int check_tensors(const char* fn, const void* q, const void* k_loc, const void* v_loc,
+                  const void* k_cmp, const void* v_cmp, const float* a, const int32_t* coords,
+                  const int32_t* cell_to_pos, const float* gate_logits, const void* last,
+                  const char* last_name = "out") {
+  return check_aligned(fn, {{q, "q"}, {k_loc, "k_loc"}, {v_loc, "v_loc"}, {k_cmp, "k_cmp"},
+                            {v_cmp, "v_cmp"}, {a, "a"}, {coords, "coords"},
+                            {cell_to_pos, "cell_to_pos"}, {gate_logits, "gate_logits"},
+                            {last, last_name}});
+}
+
 int check_buffer(void* p, size_t have, size_t need, const char* fn, const char* what) {
   if (!p) return fail(PACK3D_ERR_WORKSPACE, "%s: %s is NULL", fn, what);
   if (have < need)
@@ -245,6 +272,7 @@ int pack3d_rope(const pack3d_problem* prob, const void* x, void* y, int32_t n_he
   if (rc) return rc;
   if (!x || !y || !coords) return fail(PACK3D_ERR_NULL, "pack3d_rope: NULL tensor argument");
   if (n_heads < 1) return fail(PACK3D_ERR_SHAPE, "pack3d_rope: n_heads = %d", n_heads);
+  if ((rc = check_aligned("pack3d_rope", {{x, "x"}, {y, "y"}, {coords, "coords"}}))) return rc;
   return hip_status(launch_rope(g, x, y, n_heads, coords, (hipStream_t)stream), "k_rope");
 }
 
@@ -256,6 +284,10 @@ int pack3d_block_summary(const pack3d_problem* prob, const void* k_cmp, const vo
   if (rc) return rc;
   if (!k_cmp || !v_cmp || !cell_to_pos || !k_sum || !v_sum)
     return fail(PACK3D_ERR_NULL, "pack3d_block_summary: NULL tensor argument");
+  if ((rc = check_aligned("pack3d_block_summary",
+                          {{k_cmp, "k_cmp"}, {v_cmp, "v_cmp"}, {a, "a"},
+                           {cell_to_pos, "cell_to_pos"}, {k_sum, "k_sum"}, {v_sum, "v_sum"}})))
+    return rc;
   return hip_status(launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum, 1.0f,
                                          nullptr, (hipStream_t)stream),
                     "k_block_summary");
@@ -271,6 +303,10 @@ int pack3d_local_attn(const pack3d_problem* prob, const void* q_rot, const void*
     return fail(PACK3D_ERR_NULL, "pack3d_local_attn: NULL tensor argument");
   if (!local_supported(g))
     return fail(PACK3D_ERR_UNSUPPORTED, "pack3d_local_attn: Hq/Hkv = %d unsupported", g.G);
+  if ((rc = check_aligned("pack3d_local_attn",
+                          {{q_rot, "q_rot"}, {k_rot, "k_rot"}, {v, "v"},
+                           {cell_to_pos, "cell_to_pos"}, {o_loc, "o_loc"}, {lse_loc, "lse_loc"}})))
+    return rc;
   return hip_status(
       launch_local_attn(g, q_rot, k_rot, v, cell_to_pos, o_loc, lse_loc, (hipStream_t)stream),
       "k_local_attn");
@@ -285,6 +321,10 @@ int pack3d_global_attn(const pack3d_problem* prob, const void* q_rot, const void
   if (!q_rot || !k_sum || !v_sum || !o_cmp)
     return fail(PACK3D_ERR_NULL, "pack3d_global_attn: NULL tensor argument");
   if (m < 1) return fail(PACK3D_ERR_SHAPE, "pack3d_global_attn: m = %d must be >= 1", m);
+  if ((rc = check_aligned("pack3d_global_attn", {{q_rot, "q_rot"}, {k_sum, "k_sum"},
+                                                 {v_sum, "v_sum"}, {o_cmp, "o_cmp"},
+                                                 {lse_cmp, "lse_cmp"}})))
+    return rc;
   return hip_status(launch_global_attn(g, q_rot, k_sum, v_sum, m, nullptr, o_cmp, lse_cmp,
                                        nullptr, nullptr, nullptr, (hipStream_t)stream),
                     "k_global_attn");
@@ -297,43 +337,49 @@ int pack3d_gate_mix(const pack3d_problem* prob, const float* o_loc, const float*
   if (rc) return rc;
   if (!o_loc || !o_cmp || !gate_logits || !out)
     return fail(PACK3D_ERR_NULL, "pack3d_gate_mix: NULL tensor argument");
+  if ((rc = check_aligned("pack3d_gate_mix", {{o_loc, "o_loc"}, {o_cmp, "o_cmp"},
+                                              {gate_logits, "gate_logits"}, {out, "out"}})))
+    return rc;
   return hip_status(launch_gate_mix(g, o_loc, o_cmp, gate_logits, out, (hipStream_t)stream),
                     "k_gate_mix");
 }
 
 }  // extern "C"
 
-namespace {
+namespace pack3d {
 
-// The forward's launch sequence; with `ev` (PACK3D_FORWARD_STAGES + 1 events)
-// an event is recorded on the stream before the first stage and after each.
-int forward_impl(const pack3d_problem* prob, const void* q, const void* k_loc, const void* v_loc,
-                 const void* k_cmp, const void* v_cmp, const float* a, const int32_t* coords,
-                 const int32_t* cell_to_pos, const float* gate_logits, void* out,
-                 void* workspace, size_t ws_bytes, void* stream, void* const* ev, int32_t nev) {
-  Geom g;
-  int rc = make_geom(prob, &g);
+int api_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+// Host checks of the forward's arguments (everything but the workspace).
+int forward_check(const char* fn, const pack3d_problem* prob, const FwdArgs& x, Geom* g) {
+  int rc = make_geom(prob, g);
   if (rc) return rc;
-  if (!q || !k_loc || !v_loc || !k_cmp || !v_cmp || !coords || !cell_to_pos || !gate_logits ||
-      !out)
-    return fail(PACK3D_ERR_NULL, "pack3d_forward: NULL tensor argument");
-  if (!local_supported(g))
-    return fail(PACK3D_ERR_UNSUPPORTED, "pack3d_forward: Hq/Hkv = %d unsupported", g.G);
+  if (!x.q || !x.k_loc || !x.v_loc || !x.k_cmp || !x.v_cmp || !x.coords || !x.cell_to_pos ||
+      !x.gate || !x.out)
+    return fail(PACK3D_ERR_NULL, "%s: NULL tensor argument", fn);
+  if (!local_supported(*g))
+    return fail(PACK3D_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d unsupported", fn, g->G);
+  return check_tensors(fn, x.q, x.k_loc, x.v_loc, x.k_cmp, x.v_cmp, x.a, x.coords,
+                       x.cell_to_pos, x.gate, x.out);
+}
+
+size_t forward_workspace_bytes(const Geom& g) { return ws_layout(g).total; }
+
+// The forward's launch sequence on a checked problem and a workspace of at
+// least forward_workspace_bytes(g) bytes (256-byte aligned); with `ev`
+// (PACK3D_FORWARD_STAGES + 1 events) an event is recorded on the stream
+// before the first stage and after each.
+int forward_launch(const Geom& g, const FwdArgs& x, void* workspace, hipStream_t s,
+                   void* const* ev) {
   const WsLayout w = ws_layout(g);
-  if (!workspace) return fail(PACK3D_ERR_WORKSPACE, "pack3d_forward: workspace is NULL");
-  if (ws_bytes < w.total)
-    return fail(PACK3D_ERR_WORKSPACE, "pack3d_forward: workspace %zu bytes < %zu needed", ws_bytes,
-                w.total);
-  if ((uintptr_t)workspace & 255)
-    return fail(PACK3D_ERR_WORKSPACE, "pack3d_forward: workspace not 256-byte aligned");
-  if (ev) {
-    if (nev != PACK3D_FORWARD_STAGES + 1)
-      return fail(PACK3D_ERR_SHAPE, "pack3d_forward_timed: %d events, need %d", nev,
-                  PACK3D_FORWARD_STAGES + 1);
-    for (int i = 0; i < nev; ++i)
-      if (!ev[i]) return fail(PACK3D_ERR_NULL, "pack3d_forward_timed: event %d is NULL", i);
-  }
-  hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   void* q_rot = ws + w.q_rot;
   void* k_rot = ws + w.k_rot;
@@ -348,29 +394,55 @@ int forward_impl(const pack3d_problem* prob, const void* q, const void* k_loc, c
   };
   hipError_t e;
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  if ((e = launch_rope(g, q, q_rot, g.Hq, coords, s)) != hipSuccess) return hip_status(e, "k_rope(q)");
+  if ((e = launch_rope(g, x.q, q_rot, g.Hq, x.coords, s)) != hipSuccess)
+    return hip_status(e, "k_rope(q)");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  if ((e = launch_rope(g, k_loc, k_rot, g.Hkv, coords, s)) != hipSuccess)
+  if ((e = launch_rope(g, x.k_loc, k_rot, g.Hkv, x.coords, s)) != hipSuccess)
     return hip_status(e, "k_rope(k_loc)");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   // summaries scaled into log2-domain logits, with their norms for the
   // softmax bound of the query->summary kernel
-  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
+  if ((e = launch_block_summary(g, x.k_cmp, x.v_cmp, x.a, x.cell_to_pos, k_sum, v_sum,
                                 g.scale * 1.4426950408889634f, knorm, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, nullptr, s)) != hipSuccess)
+  if ((e = launch_local_attn(g, q_rot, k_rot, x.v_loc, x.cell_to_pos, o_loc, nullptr, s)) !=
+      hipSuccess)
     return hip_status(e, "k_local_attn");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   // the compressed branch's query: rotated, or the input q when it is blind
-  const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? q : q_rot;
-  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, nullptr, nullptr, o_loc, gate_logits,
-                         out, s);
+  const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? x.q : q_rot;
+  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, nullptr, nullptr, o_loc, x.gate,
+                         x.out, s);
   if (e != hipSuccess) return hip_status(e, "k_global_attn(gated)");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   return ok();
+}
+
+}  // namespace pack3d
+
+namespace {
+
+int forward_impl(const char* fn, const pack3d_problem* prob, const FwdArgs& x, void* workspace,
+                 size_t ws_bytes, void* stream, void* const* ev, int32_t nev) {
+  Geom g;
+  int rc = forward_check(fn, prob, x, &g);
+  if (rc) return rc;
+  const size_t need = forward_workspace_bytes(g);
+  if (!workspace) return fail(PACK3D_ERR_WORKSPACE, "%s: workspace is NULL", fn);
+  if (ws_bytes < need)
+    return fail(PACK3D_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  if ((uintptr_t)workspace & 255)
+    return fail(PACK3D_ERR_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
+  if (ev) {
+    if (nev != PACK3D_FORWARD_STAGES + 1)
+      return fail(PACK3D_ERR_SHAPE, "%s: %d events, need %d", fn, nev, PACK3D_FORWARD_STAGES + 1);
+    for (int i = 0; i < nev; ++i)
+      if (!ev[i]) return fail(PACK3D_ERR_NULL, "%s: event %d is NULL", fn, i);
+  }
+  return forward_launch(g, x, workspace, (hipStream_t)stream, ev);
 }
 
 }  // namespace
@@ -381,8 +453,8 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
                    const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
                    const int32_t* coords, const int32_t* cell_to_pos, const float* gate_logits,
                    void* out, void* workspace, size_t ws_bytes, void* stream) {
-  return forward_impl(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits,
-                      out, workspace, ws_bytes, stream, nullptr, 0);
+  const FwdArgs x{q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits, out};
+  return forward_impl("pack3d_forward", prob, x, workspace, ws_bytes, stream, nullptr, 0);
 }
 
 int pack3d_forward_timed(const pack3d_problem* prob, const void* q, const void* k_loc,
@@ -391,8 +463,9 @@ int pack3d_forward_timed(const pack3d_problem* prob, const void* q, const void* 
                          const float* gate_logits, void* out, void* workspace, size_t ws_bytes,
                          void* stream, void* const* events, int32_t n_events) {
   if (!events) return fail(PACK3D_ERR_NULL, "pack3d_forward_timed: events is NULL");
-  return forward_impl(prob, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits,
-                      out, workspace, ws_bytes, stream, events, n_events);
+  const FwdArgs x{q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits, out};
+  return forward_impl("pack3d_forward_timed", prob, x, workspace, ws_bytes, stream, events,
+                      n_events);
 }
 
 int pack3d_build_cell_index(const pack3d_problem* prob, const int32_t* coords,
@@ -402,6 +475,9 @@ int pack3d_build_cell_index(const pack3d_problem* prob, const int32_t* coords,
   if (rc) return rc;
   if (!coords || !cell_to_pos)
     return fail(PACK3D_ERR_NULL, "pack3d_build_cell_index: NULL tensor argument");
+  if ((rc = check_aligned("pack3d_build_cell_index",
+                          {{coords, "coords"}, {cell_to_pos, "cell_to_pos"}})))
+    return rc;
   return hip_status(launch_build_cell_index(g, coords, cell_to_pos, (hipStream_t)stream),
                     "k_cell_index");
 }
@@ -413,6 +489,11 @@ int pack3d_check_packing(const pack3d_problem* prob, const int32_t* coords,
   if (rc) return rc;
   if (!coords || !cell_to_pos || !n_bad_dev)
     return fail(PACK3D_ERR_NULL, "pack3d_check_packing: NULL tensor argument");
+  if ((rc = check_aligned("pack3d_check_packing",
+                          {{coords, "coords"}, {cell_to_pos, "cell_to_pos"}})))
+    return rc;
+  if ((uintptr_t)n_bad_dev & 3)
+    return fail(PACK3D_ERR_SHAPE, "pack3d_check_packing: n_bad_dev is not 4-byte aligned");
   return hip_status(launch_check_packing(g, coords, cell_to_pos, n_bad_dev, (hipStream_t)stream),
                     "k_check_packing");
 }
@@ -447,6 +528,9 @@ int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* 
     return fail(PACK3D_ERR_NULL, "%s: NULL tensor argument", fn);
   if (!local_supported(g))
     return fail(PACK3D_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d unsupported", fn, g.G);
+  if ((rc = check_tensors(fn, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits,
+                          out)))
+    return rc;
   const WsLayout w = ws_layout(g);
   const SavedLayout sl = saved_layout(g);
   if ((rc = check_buffer(workspace, ws_bytes, w.total, fn, "workspace"))) return rc;
@@ -498,6 +582,11 @@ int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc
     return fail(PACK3D_ERR_UNSUPPORTED,
                 "%s: only bf16 with Hq/Hkv in {4, 8, 16} is supported (dtype %d, Hq/Hkv %d)", fn,
                 prob->dtype, g.G);
+  if ((rc = check_tensors(fn, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell_to_pos, gate_logits,
+                          dout, "dout")) ||
+      (rc = check_aligned(fn, {{dq, "dq"}, {dk_loc, "dk_loc"}, {dv_loc, "dv_loc"},
+                               {dk_cmp, "dk_cmp"}, {dv_cmp, "dv_cmp"}, {dgate, "dgate"}})))
+    return rc;
   const BwdLayout w = bwd_layout(g);
   const SavedLayout sl = saved_layout(g);
   if ((rc = check_buffer(workspace, ws_bytes, w.total, fn, "workspace"))) return rc;
@@ -608,6 +697,11 @@ int pack3d_layernorm_qkv(const pack3d_problem* prob, int32_t width, const void* 
   if (!h || !w_qkv || !coords || !x_norm || !q_rot || !k_rot || !v_loc || !k_cmp || !v_cmp)
     return fail(PACK3D_ERR_NULL, "%s: NULL tensor argument", fn);
   if (!(eps > 0.0f) || !isfinite(eps)) return fail(PACK3D_ERR_SHAPE, "%s: eps must be > 0", fn);
+  if ((rc = check_aligned(fn, {{h, "h"}, {gamma, "gamma"}, {beta, "beta"}, {w_qkv, "w_qkv"},
+                               {coords, "coords"}, {x_norm, "x_norm"}, {q_rot, "q_rot"},
+                               {q_raw, "q_raw"}, {k_rot, "k_rot"}, {v_loc, "v_loc"},
+                               {k_cmp, "k_cmp"}, {v_cmp, "v_cmp"}})))
+    return rc;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = launch_layernorm(g, width, h, gamma, beta, eps, x_norm, s)) != hipSuccess)
@@ -624,6 +718,8 @@ int pack3d_out_proj(const pack3d_problem* prob, int32_t width, const void* o, co
   int rc = make_geom(prob, &g);
   if (rc || (rc = check_width(g, width, fn))) return rc;
   if (!o || !w_o || !residual || !out) return fail(PACK3D_ERR_NULL, "%s: NULL tensor argument", fn);
+  if ((rc = check_aligned(fn, {{o, "o"}, {w_o, "w_o"}, {residual, "residual"}, {out, "out"}})))
+    return rc;
   return hip_status(launch_out_proj(g, width, o, w_o, residual, out, (hipStream_t)stream),
                     "k_gemm<residual>");
 }
@@ -649,6 +745,11 @@ int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* 
   if (!(eps > 0.0f) || !isfinite(eps)) return fail(PACK3D_ERR_SHAPE, "%s: eps must be > 0", fn);
   if (!local_supported(g))
     return fail(PACK3D_ERR_UNSUPPORTED, "%s: Hq/Hkv = %d unsupported", fn, g.G);
+  if ((rc = check_aligned(fn, {{h, "h"}, {gamma, "gamma"}, {beta, "beta"}, {w_qkv, "w_qkv"},
+                               {w_o, "w_o"}, {a, "a"}, {coords, "coords"},
+                               {cell_to_pos, "cell_to_pos"}, {gate_logits, "gate_logits"},
+                               {out, "out"}})))
+    return rc;
   const LayerLayout w = layer_layout(g, width);
   if ((rc = check_buffer(workspace, ws_bytes, w.total, fn, "workspace"))) return rc;
   hipStream_t s = (hipStream_t)stream;

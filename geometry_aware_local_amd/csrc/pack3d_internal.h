@@ -118,4 +118,26 @@ hipError_t launch_build_cell_index(const Geom& g, const int32_t* coords, int32_t
 hipError_t launch_check_packing(const Geom& g, const int32_t* coords, const int32_t* c2p,
                                 int32_t* n_bad, hipStream_t s);
 
+// The forward's tensors, as pack3d_forward takes them.
+struct FwdArgs {
+  const void *q, *k_loc, *v_loc, *k_cmp, *v_cmp;
+  const float* a;
+  const int32_t *coords, *cell_to_pos;
+  const float* gate;
+  void* out;
+};
+
+// Sets the calling thread's pack3d_last_error() text and returns `code`.
+int api_fail(int code, const char* fmt, ...);
+// Host checks of the forward's problem and tensors (not its workspace);
+// fills *g.  `fn` names the entry point in error messages.
+int forward_check(const char* fn, const pack3d_problem* prob, const FwdArgs& x, Geom* g);
+// Workspace bytes of the forward for a checked problem.
+size_t forward_workspace_bytes(const Geom& g);
+// The forward's launches on a checked problem with a workspace of at least
+// forward_workspace_bytes(g) bytes (256-byte aligned); `ev`: NULL or
+// PACK3D_FORWARD_STAGES + 1 events recorded around the stages.
+int forward_launch(const Geom& g, const FwdArgs& x, void* workspace, hipStream_t s,
+                   void* const* ev);
+
 }  // namespace pack3d

@@ -402,12 +402,22 @@ def pack3d_backward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cel
     return g
 
 
-def pack3d_build_cell_index(prob: Problem, coords: torch.Tensor) -> torch.Tensor:
+def pack3d_build_cell_index(prob: Problem, coords: torch.Tensor,
+                            check: bool = True) -> torch.Tensor:
+    """cell_to_pos for ``coords``.  Cells no token maps to keep -1; with
+    ``check`` (the default; it synchronises) the index is verified with
+    pack3d_check_packing and ``ValueError`` is raised unless coords is a
+    bijection onto the lattice, since the kernels dereference every entry."""
     n = prob.n_tokens
-    c2p = torch.empty(n, dtype=torch.int32, device=coords.device)
+    c2p = torch.full((n,), -1, dtype=torch.int32, device=coords.device)
     _check(LIB.pack3d_build_cell_index(ctypes.byref(prob),
                                         _ptr(coords, torch.int32, (n, 3), "coords"),
                                         c2p.data_ptr(), _stream(coords.device)))
+    if check:
+        bad = pack3d_check_packing(prob, coords, c2p)
+        if bad:
+            raise ValueError(f"coords is not a bijection onto the lattice: {bad} tokens are "
+                             "outside it or share a cell")
     return c2p
 
 

@@ -21,6 +21,10 @@
  * - Arrays are dense, row-major, contiguous, device memory (HBM), owned by
  *   the caller.  The library never allocates device memory and keeps no
  *   state between calls except a per-thread error string.
+ * - Every array argument must start on a 16-byte boundary (the kernels move
+ *   rows with 16-byte vector and direct-to-LDS copies); a misaligned pointer
+ *   is rejected with PACK3D_ERR_SHAPE before any launch.  Workspaces and the
+ *   saved state need 256-byte alignment (PACK3D_ERR_WORKSPACE).
  * - "dtype" arrays hold float (PACK3D_F32) or bf16 (PACK3D_BF16) values as
  *   chosen by pack3d_problem.dtype.  Accumulation is always fp32.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
@@ -311,9 +315,12 @@ size_t pack3d_layer_workspace_size(const pack3d_problem* prob, int32_t width);
 /* Bytes of workspace pack3d_forward needs for this problem (0 if invalid). */
 size_t pack3d_forward_workspace_size(const pack3d_problem* prob);
 
-/* cell_to_pos[(z*Y + y)*X + x] = i for every i < N (coords must be a
- * bijection onto the lattice; entries of cells no token maps to are left
- * unwritten). */
+/* cell_to_pos[(z*Y + y)*X + x] = i for every i < N.  Tokens whose
+ * coordinates lie outside the lattice are skipped, and entries of cells no
+ * token maps to are left unwritten, so the result is a valid index (one the
+ * kernels may dereference) only when coords is a bijection onto the lattice:
+ * fill cell_to_pos with -1 first and call pack3d_check_packing(), which must
+ * report 0, before passing it to any other entry point. */
 int pack3d_build_cell_index(const pack3d_problem* prob, const int32_t* coords,
                             int32_t* cell_to_pos, void* stream);
 

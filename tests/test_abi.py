@@ -211,3 +211,41 @@ def test_layer_workspace_layout(pk):
     assert pk.pack3d_layer_workspace_size(p, 512) == want
     pb = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1, summary_mode="blind")
     assert pk.pack3d_layer_workspace_size(pb, 512) == want + a256(2 * n * hq * 64)
+
+
+def test_misaligned_tensors_are_rejected_on_the_host(pk):
+    """Every array argument must start on a 16-byte boundary; a misaligned
+    pointer (a fake address, never dereferenced) is rejected with
+    PACK3D_ERR_SHAPE before any launch, naming the argument."""
+    L = pk.LIB
+    p = _prob(pk, n_q_heads=8, n_kv_heads=2)
+    b = ctypes.byref(p)
+    big = 10 ** 12
+    bad = FAKE + 8                                         # 8-byte aligned only
+    assert L.pack3d_rope(b, FAKE, bad, 2, FAKE, None) == -2
+    assert "y is not 16-byte aligned" in pk.pack3d_last_error()
+    assert L.pack3d_block_summary(b, FAKE, FAKE, bad, FAKE, FAKE, FAKE, None) == -2
+    assert "a is not" in pk.pack3d_last_error()
+    assert L.pack3d_local_attn(b, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None, None) == -2
+    assert L.pack3d_global_attn(b, FAKE + 2, FAKE, FAKE, 64, FAKE, None, None) == -2
+    assert L.pack3d_gate_mix(b, FAKE, FAKE, FAKE, bad, None) == -2
+    assert L.pack3d_build_cell_index(b, bad, FAKE, None) == -2
+    assert L.pack3d_check_packing(b, FAKE, FAKE, FAKE + 2, None) == -2
+    fwd = [FAKE] * 10                                      # q .. out
+    for i in range(10):
+        args = list(fwd)
+        args[i] = bad
+        assert L.pack3d_forward(b, *args, FAKE, big, None) == -2, i
+        assert "16-byte aligned" in pk.pack3d_last_error()
+        assert L.pack3d_forward_train(b, *args, FAKE, big, FAKE, big, None) == -2, i
+    inp = [FAKE] * 9                                       # q .. gate
+    outs = [FAKE] * 6                                      # dq .. dgate
+    assert L.pack3d_backward(b, *inp, FAKE, big, bad, *outs, FAKE, big, None) == -2
+    assert "dout" in pk.pack3d_last_error()
+    outs[5] = bad
+    assert L.pack3d_backward(b, *inp, FAKE, big, FAKE, *outs, FAKE, big, None) == -2
+    assert "dgate" in pk.pack3d_last_error()
+    pbf = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1)
+    assert L.pack3d_out_proj(ctypes.byref(pbf), 512, FAKE, FAKE, bad, FAKE, None) == -2
+    assert "residual" in pk.pack3d_last_error()
+

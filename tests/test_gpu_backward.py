@@ -95,6 +95,8 @@ def test_backward_small(pk, w):
                        inp.gate, dout)
     errs = {n: _rel(gu.host(g[n]), ref[n]) for n in NAMES}
     _say("  rel errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    _say("  abs errors", {n: f"{gu.max_abs(gu.host(g[n]), ref[n]):.2e}" for n in NAMES},
+         "max |ref|", {n: f"{np.abs(ref[n]).max():.2e}" for n in NAMES})
     for n in NAMES:
         assert errs[n] <= GRAD_TOL, n
     # the training forward: same output as the forward, saved state = the
@@ -197,6 +199,8 @@ def test_backward_262k_sampled(pk):
                                               q_is_rows=True)
     dq_c, _, _ = orc.global_attention_backward(f["q_rot"], f["k_sum"], f["v_sum"], tau, d_cmp)
     dq = orc.rotate_transpose(dq_l + dq_c, inp.coords[rows], w.rope_pairs, w.rope_base)
+    _say(f"  dq abs {gu.max_abs(got['dq'][rows], dq):.2e} (max |ref| {np.abs(dq).max():.2e}), "
+         f"dgate abs {gu.max_abs(got['dgate'][rows], dg):.2e} (max |ref| {np.abs(dg).max():.2e})")
     assert _rel(got["dq"][rows], dq) <= GRAD_TOL
     assert _rel(got["dgate"][rows], dg) <= GRAD_TOL
     # --- sampled keys: every query of each key's window
@@ -211,6 +215,9 @@ def test_backward_262k_sampled(pk):
                                                w.grid, w.window, tau, d_loc2, near,
                                                q_is_rows=True)
     dk = orc.rotate_transpose(dk_r[keys], inp.coords[keys], w.rope_pairs, w.rope_base)
+    _say(f"  dk_loc abs {gu.max_abs(got['dk_loc'][keys], dk):.2e} "
+         f"(max |ref| {np.abs(dk).max():.2e}), dv_loc abs "
+         f"{gu.max_abs(got['dv_loc'][keys], dv[keys]):.2e} (max |ref| {np.abs(dv[keys]).max():.2e})")
     assert _rel(got["dk_loc"][keys], dk) <= GRAD_TOL
     assert _rel(got["dv_loc"][keys], dv[keys]) <= GRAD_TOL
     # --- summary path, at any size: sum_u dv_cmp[u, g] = sum over the

@@ -1,11 +1,12 @@
 """GPU parity: every libpack3d entry point against the fp64 oracle.
 
 The HIP path is called through the C ABI (ctypes binding); expected values come
-from ``oracle/`` only.  Small workloads are compared element by element in
-full; the 262 144- and 1 048 576-token workloads on sampled query rows.
+from ``oracle/`` only.  Small workloads and the 65 536-token workload are
+compared element by element in full; the 262 144-, 1 048 576-, 4 194 304- and
+8 388 608-token workloads on sampled query rows.  The fused forward (the path
+the bench times) is checked branch by branch through the training forward,
+which launches the same kernels and also saves each branch's output.
 """
-
-import os
 
 import numpy as np
 import pytest
@@ -174,11 +175,34 @@ def test_gate_mix(pk, w, per_head):
 # the whole path
 # --------------------------------------------------------------------------
 
+def _fargs(pk, w, d, **kw):
+    return (gu.problem(pk, w, **kw), d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"],
+            d["a"], d["coords"], d["cell_to_pos"], d["gate"])
+
+
+def _check_fused_branches(pk, prob, fargs, out, ref, rows, dtype):
+    """The fused forward the bench times (pre-scaled summaries, the
+    per-group norm bound, the gated epilogue) checked branch by branch: the
+    training forward launches the same kernels, gives the same output bit
+    for bit and also saves each branch's fp32 output."""
+    out_t, saved = pk.pack3d_forward_train(*fargs)
+    sv = pk.saved_views(prob, saved)
+    assert torch.equal(out_t, out)
+    idx = torch.from_numpy(np.asarray(rows, np.int64)).cuda()
+    o_loc = gu.host(sv["o_loc"][idx])
+    o_cmp = gu.host(sv["o_cmp"][idx])
+    e_loc, e_cmp = gu.max_rel(o_loc, ref["o_loc"]), gu.max_rel(o_cmp, ref["o_cmp"])
+    _say(f"  fused branches: o_loc rel {e_loc:.2e}, o_cmp rel {e_cmp:.2e} "
+         f"(max |o_cmp| {np.abs(ref['o_cmp']).max():.3e})")
+    assert e_loc <= gu.REL_TOL[dtype]
+    assert e_cmp <= gu.REL_TOL[dtype]
+
+
 def _check_forward(pk, w, inp, rows):
     d = gu.device_inputs(inp)
-    prob = gu.problem(pk, w)
-    out = pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"],
-                            d["coords"], d["cell_to_pos"], d["gate"])
+    fargs = _fargs(pk, w, d)
+    prob = fargs[0]
+    out = pk.pack3d_forward(*fargs)
     # the same chain through the split entry points, for per-branch checks
     q_rot = pk.pack3d_rope(prob, d["q"], d["coords"])
     k_rot = pk.pack3d_rope(prob, d["k_loc"], d["coords"])
@@ -189,9 +213,12 @@ def _check_forward(pk, w, inp, rows):
     ref = orc.forward(w, inp.q, inp.k_loc, inp.v_loc, inp.k_cmp, inp.v_cmp, inp.a, inp.coords,
                       inp.gate, rows=rows)
     got = gu.host(out)[rows]
-    assert gu.max_abs(got, ref["out"]) <= gu.ABS_TOL[w.dtype]
+    err = gu.max_abs(got, ref["out"])
+    _say(f"  out max abs {err:.2e} over {len(rows)} rows")
+    assert err <= gu.ABS_TOL[w.dtype]
     assert gu.max_rel(gu.host(o_loc)[rows], ref["o_loc"]) <= gu.REL_TOL[w.dtype]
     assert gu.max_rel(gu.host(o_cmp)[rows], ref["o_cmp"]) <= gu.REL_TOL[w.dtype]
+    _check_fused_branches(pk, prob, fargs, out, ref, rows, w.dtype)
     # the split chain's gate gives the fused forward's result
     mixed = pk.pack3d_gate_mix(prob, o_loc, o_cmp, d["gate"])
     assert gu.max_abs(gu.host(mixed), gu.host(out)) <= (1e-6 if w.dtype == "f32" else 1e-2)
@@ -205,10 +232,11 @@ def test_forward_small(pk, w):
     _check_forward(pk, w, inp, np.arange(w.n_tokens))
 
 
-def test_forward_65k_morton(pk):
-    _say("forward", MORTON.name)
+def test_forward_65k_morton_full(pk):
+    """The 65 536-token Morton workload compared in full: every row, every head."""
+    _say("forward", MORTON.name, "all rows")
     inp = sg.make_inputs(MORTON)
-    _check_forward(pk, MORTON, inp, _rows(MORTON, 4096))
+    _check_forward(pk, MORTON, inp, np.arange(MORTON.n_tokens))
 
 
 def test_branches_with_peaked_queries(pk):
@@ -300,32 +328,91 @@ def _reach(pk, w, nrows):
     assert gu.max_abs(got, ref["out"]) <= gu.ABS_TOL["bf16"]
 
 
-REACH = pytest.mark.skipif(os.environ.get("PACK3D_REACH") != "1",
-                           reason="reach sizes take minutes of host time for the inputs and "
-                                  "the oracle's summaries; set PACK3D_REACH=1")
-
-
-@REACH
 def test_forward_4m_reach_sampled(pk):
     _reach(pk, W["reach_bf16_64x256x256"], 64)
 
 
-@REACH
 def test_forward_8m_reach_sampled(pk):
     _reach(pk, W["reach_bf16_128x256x256"], 64)
 
 
 def test_forward_1m_random_sampled(pk):
+    """1 048 576 tokens in random packing (M = 65 536): the end-to-end bound
+    and both branches of the fused path against the relative bound, on
+    sampled rows.  At this size the compressed branch is far below the
+    absolute bound, so only the per-branch check could see it break."""
     _say("forward", RANDOM.name)
     inp = sg.make_inputs(RANDOM)
-    rows = _rows(RANDOM, 256, seed=3)
+    rows = _rows(RANDOM, 512, seed=3)
     d = gu.device_inputs(inp)
-    prob = gu.problem(pk, RANDOM)
-    out = pk.pack3d_forward(prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"],
-                            d["coords"], d["cell_to_pos"], d["gate"])
+    fargs = _fargs(pk, RANDOM, d)
+    out = pk.pack3d_forward(*fargs)
     ref = orc.forward(RANDOM, inp.q, inp.k_loc, inp.v_loc, inp.k_cmp, inp.v_cmp, inp.a,
                       inp.coords, inp.gate, rows=rows)
-    assert gu.max_abs(gu.host(out)[rows], ref["out"]) <= gu.ABS_TOL["bf16"]
+    err = gu.max_abs(gu.host(out)[rows], ref["out"])
+    _say(f"  out max abs {err:.2e}")
+    assert err <= gu.ABS_TOL["bf16"]
+    _check_fused_branches(pk, fargs[0], fargs, out, ref, rows, "bf16")
+
+
+def test_dense_companion_1m_sampled(pk):
+    """The dense axial-RoPE attention the bench times beside the forward at
+    1 048 576 tokens: 1x1x1 blocks with a = 1 make the compressed branch
+    attend to every rotated key (m = N), checked on sampled rows against the
+    oracle's dense softmax over all N keys."""
+    w = RANDOM
+    _say("dense companion", w.name)
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    dprob = gu.problem(pk, w.with_(block=(1, 1, 1)))
+    q_rot = pk.pack3d_rope(prob, d["q"], d["coords"])
+    dk, dv = pk.pack3d_block_summary(dprob, d["k_cmp"], d["v_cmp"], None, d["cell_to_pos"])
+    assert dk.shape[1] == w.n_tokens
+    o = pk.pack3d_global_attn(dprob, q_rot, dk, dv)
+    rows = _rows(w, 48, seed=6)
+    got = gu.host(o[torch.from_numpy(rows).cuda()])
+    del o, dk, dv, q_rot, d
+    torch.cuda.empty_cache()
+    qr = orc.rotate(inp.q[rows], inp.coords[rows])
+    rk, rv = orc.block_summaries(inp.k_cmp, inp.v_cmp, None, inp.coords, w.grid, (1, 1, 1))
+    ref, _ = orc.global_attention(qr, rk, rv, 0.125, q_is_rows=True)
+    e_abs, e_rel = gu.max_abs(got, ref), gu.max_rel(got, ref)
+    _say(f"  max abs {e_abs:.2e}, rel {e_rel:.2e}")
+    assert e_abs <= gu.ABS_TOL["bf16"]
+    assert e_rel <= gu.REL_TOL["bf16"]
+
+
+# End-to-end error against the logit scale.  The GPU rounds the rotated q, k
+# (and the summaries) to bf16 before the products, so each logit carries an
+# error that grows with |q||k|; queries scaled by s multiply every logit by s.
+# Measured maximum abs errors of the output against the fp64 oracle are
+# printed for every scale; the end-to-end bound is asserted up to
+# PEAKED_MAX_SCALE.
+PEAKED_SCALES = (1.0, 2.0, 3.0, 4.0)
+PEAKED_MAX_SCALE = 2.0
+
+
+@pytest.mark.parametrize("qscale", PEAKED_SCALES)
+def test_forward_end_to_end_logit_scale(pk, qscale):
+    w = MORTON.with_(grid=(8, 32, 32))
+    _say("forward logit scale", qscale, w.name)
+    inp = sg.make_inputs(w)
+    inp.q = sg.round_to_bf16((inp.q * qscale).astype(np.float32))
+    d = gu.device_inputs(inp)
+    fargs = _fargs(pk, w, d)
+    out = pk.pack3d_forward(*fargs)
+    rows = np.arange(w.n_tokens)
+    ref = orc.forward(w, inp.q, inp.k_loc, inp.v_loc, inp.k_cmp, inp.v_cmp, inp.a, inp.coords,
+                      inp.gate, rows=rows)
+    out_t, saved = pk.pack3d_forward_train(*fargs)
+    sv = pk.saved_views(fargs[0], saved)
+    e = gu.max_abs(gu.host(out), ref["out"])
+    e_loc = gu.max_abs(gu.host(sv["o_loc"]), ref["o_loc"])
+    e_cmp = gu.max_abs(gu.host(sv["o_cmp"]), ref["o_cmp"])
+    _say(f"  scale {qscale}: out max abs {e:.3e}; o_loc {e_loc:.3e}; o_cmp {e_cmp:.3e}")
+    if qscale <= PEAKED_MAX_SCALE:
+        assert e <= gu.ABS_TOL["bf16"]
 
 
 # --------------------------------------------------------------------------

@@ -178,6 +178,51 @@ def test_value_summaries_closed_form_with_zero_keys():
     assert np.abs(lse - math.log(w.n_blocks)).max() <= 1e-12
 
 
+def test_value_summaries_with_softmax_weights():
+    """v~_j is the a-weighted sum of the values of block j's cells, with each
+    KV group's own weights (notes, key design 2, the equation for v~_j: a
+    normalised weighted average).  Pinned two ways on a randomly packed
+    lattice with two KV groups and per-group softmax weights:
+    * brute force: block members found by scanning the lattice, summed with
+      their weights one by one;
+    * a closed form at any size: K_cmp = 0 makes every query->summary logit 0,
+      so o_cmp is the mean over j of v~_j, i.e. (1/M) sum_u a_u v_u over all
+      tokens of the group (no block membership involved).
+    Plausible mistakes (pooling V uniformly, or with the other group's
+    weights) fail both."""
+    w = _small(grid=(2, 8, 8), hq=4, hkv=2, block=(2, 4, 4), packing="random")
+    inp = sg.make_inputs(w)
+    a = inp.a
+    assert np.abs(a[:, 0] - a[:, 1]).max() > 0.1          # the groups' weights differ
+    assert np.abs(a - 1.0 / 32).max() > 0.1                # and are far from uniform
+    _, vs = orc.block_summaries(inp.k_cmp, inp.v_cmp, a, inp.coords, w.grid, w.block)
+    members = _members_brute_force(w.grid, w.block)
+    want = np.zeros_like(vs)
+    for j, cells in enumerate(members):
+        for cell in cells:
+            u = inp.cell_to_pos[cell]
+            for g in range(w.n_kv_heads):
+                want[g, j] += a[u, g] * inp.v_cmp[u, g].astype(np.float64)
+    assert np.abs(vs - want).max() <= 1e-13
+    # the closed form through the compressed branch with zero keys
+    ks0, vs0 = orc.block_summaries(np.zeros_like(inp.k_cmp), inp.v_cmp, a, inp.coords, w.grid,
+                                   w.block)
+    o, _ = orc.global_attention(orc.rotate(inp.q, inp.coords), ks0, vs0, 0.125)
+    grp = w.n_q_heads // w.n_kv_heads
+    pooled = [(a[:, g, None] * inp.v_cmp[:, g].astype(np.float64)).sum(0) / w.n_blocks
+              for g in range(w.n_kv_heads)]
+    for h in range(w.n_q_heads):
+        assert np.abs(o[:, h] - pooled[h // grp]).max() <= 1e-13
+    # test power: the plausible mistakes are far outside both bounds
+    for bad_a in (None, np.ascontiguousarray(a[:, ::-1])):
+        _, bad = orc.block_summaries(inp.k_cmp, inp.v_cmp, bad_a, inp.coords, w.grid, w.block)
+        assert np.abs(bad - want).max() > 1e-2
+        _, bad0 = orc.block_summaries(np.zeros_like(inp.k_cmp), inp.v_cmp, bad_a, inp.coords,
+                                      w.grid, w.block)
+        ob, _ = orc.global_attention(orc.rotate(inp.q, inp.coords), ks0, bad0, 0.125)
+        assert max(np.abs(ob[:, h] - pooled[h // grp]).max() for h in range(w.n_q_heads)) > 1e-3
+
+
 def test_summaries_with_unit_blocks_are_rotated_keys():
     """With 1x1x1 blocks and a = 1 each summary is one rotated key, in raster
     cell order."""
