@@ -43,7 +43,9 @@ EXPORTS = (
     "pack3d_backend_info", "pack3d_version", "pack3d_saved_size", "pack3d_forward_train",
     "pack3d_backward_workspace_size", "pack3d_backward", "pack3d_layernorm_qkv",
     "pack3d_out_proj", "pack3d_layer_forward", "pack3d_layer_workspace_size",
+    "pack3d_forward_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 256 << 20      # PACK3D_NOALLOC_SCRATCH_BYTES
 
 
 class Pack3DError(RuntimeError):
@@ -95,6 +97,7 @@ def _load() -> ctypes.CDLL:
         "pack3d_global_attn": [P, V, V, V, I32, V, V, V],
         "pack3d_gate_mix": [P, V, V, V, V, V],
         "pack3d_forward": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V],
+        "pack3d_forward_noalloc": [P, V, V, V, V, V, V, V, V, V, V, V],
         "pack3d_forward_timed": [P, V, V, V, V, V, V, V, V, V, V, V, SZ, V,
                                  ctypes.POINTER(ctypes.c_void_p), I32],
         "pack3d_build_cell_index": [P, V, V, V],
@@ -299,6 +302,23 @@ def pack3d_forward(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords, cell
                                   gate, workspace, out)
     _check(LIB.pack3d_forward(*args))
     del ws
+    return out
+
+
+def pack3d_forward_noalloc(prob: Problem, q, k_loc, v_loc, k_cmp, v_cmp, a, coords,
+                           cell_to_pos, gate, out: torch.Tensor) -> torch.Tensor:
+    """The forward with the library's static scratch array as its workspace
+    (no device allocation in the call; ``out`` is given by the caller)."""
+    n, hq, hkv, dt = prob.n_tokens, prob.n_q_heads, prob.n_kv_heads, prob.torch_dtype
+    gshape = (n, hq, 2) if prob.gate_per_head else (n, 2)
+    _check(LIB.pack3d_forward_noalloc(
+        ctypes.byref(prob), _ptr(q, dt, (n, hq, 64), "q"),
+        _ptr(k_loc, dt, (n, hkv, 64), "k_loc"), _ptr(v_loc, dt, (n, hkv, 64), "v_loc"),
+        _ptr(k_cmp, dt, (n, hkv, 64), "k_cmp"), _ptr(v_cmp, dt, (n, hkv, 64), "v_cmp"),
+        _ptr(a, torch.float32, (n, hkv), "a"), _ptr(coords, torch.int32, (n, 3), "coords"),
+        _ptr(cell_to_pos, torch.int32, (n,), "cell_to_pos"),
+        _ptr(gate, torch.float32, gshape, "gate"), _ptr(out, dt, (n, hq, 64), "out"),
+        _stream(q.device)))
     return out
 
 

@@ -200,6 +200,29 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
                    void* stream);
 
 /*
+ * The forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, launches, kernels and result as
+ * pack3d_forward, with the workspace in a static device array of
+ * PACK3D_NOALLOC_SCRATCH_BYTES (256 MiB) that every GPU the library runs on
+ * holds until the process ends.  The call allocates nothing.
+ *   - Problems whose pack3d_forward_workspace_size() exceeds that size are
+ *     rejected with PACK3D_ERR_WORKSPACE before any launch (at 8 query heads,
+ *     2 KV groups and bf16, up to ~78 000 tokens).
+ *   - Every call on a GPU shares that GPU's array, which keeps the last
+ *     call's contents (the forward writes every part it reads, so nothing
+ *     needs clearing): calls that overlap on one GPU (different streams, no
+ *     ordering between them) race and give undefined results.
+ *   - The first call on each device looks up the array's device address
+ *     (hipGetSymbolAddress) with that device current.
+ */
+#define PACK3D_NOALLOC_SCRATCH_BYTES (256u << 20)
+int pack3d_forward_noalloc(const pack3d_problem* prob, const void* q, const void* k_loc,
+                           const void* v_loc, const void* k_cmp, const void* v_cmp,
+                           const float* a, const int32_t* coords, const int32_t* cell_to_pos,
+                           const float* gate_logits, void* out, void* stream);
+
+/*
  * pack3d_forward with per-stage timing: the same launches, plus an event
  * recorded on `stream` before the first stage and after each of the
  * PACK3D_FORWARD_STAGES stages, in this order:

@@ -249,3 +249,26 @@ def test_misaligned_tensors_are_rejected_on_the_host(pk):
     assert L.pack3d_out_proj(ctypes.byref(pbf), 512, FAKE, FAKE, bad, FAKE, None) == -2
     assert "residual" in pk.pack3d_last_error()
 
+
+def test_noalloc_forward_checks_on_the_host(pk):
+    """pack3d_forward_noalloc: NULLs, misaligned tensors and problems whose
+    workspace exceeds the static scratch array are rejected before the
+    device is touched."""
+    L = pk.LIB
+    small = _prob(pk, n_q_heads=8, n_kv_heads=2)
+    big = _prob(pk, grid=(64, 64, 64), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
+    assert pk.pack3d_forward_workspace_size(small) <= pk.NOALLOC_SCRATCH_BYTES
+    assert pk.pack3d_forward_workspace_size(big) > pk.NOALLOC_SCRATCH_BYTES
+    fwd = [FAKE] * 10
+    assert L.pack3d_forward_noalloc(ctypes.byref(big), *fwd, None) == -4
+    assert "static scratch" in pk.pack3d_last_error()
+    nul = list(fwd)
+    nul[0] = None
+    assert L.pack3d_forward_noalloc(ctypes.byref(small), *nul, None) == -1
+    mis = list(fwd)
+    mis[9] = FAKE + 8
+    assert L.pack3d_forward_noalloc(ctypes.byref(small), *mis, None) == -2
+    assert "out is not 16-byte aligned" in pk.pack3d_last_error()
+    text = open(HEADER).read()
+    assert "#define PACK3D_NOALLOC_SCRATCH_BYTES (256u << 20)" in text
+    assert pk.NOALLOC_SCRATCH_BYTES == 256 << 20
