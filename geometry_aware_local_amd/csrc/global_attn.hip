@@ -170,7 +170,7 @@ struct GCol {
 // One 64-key tile for all of the wave's column blocks.
 template <typename T, int CB, int MODE>
 __device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __restrict__ vl,
-                                       int64_t k0, int64_t m,
+                                       int k0, int m,
                                        float c, const QFrag<T> (&qf)[CB], GCol (&st)[CB],
                                        f32x16 (&o)[CB][2], int lane) {
   const int h = lane >> 5, col = lane & 31;
@@ -187,7 +187,7 @@ __device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __rest
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t key = k0 + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int key = k0 + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
         if (key >= m)
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) s[kb][cb][v] = kNegInf;
@@ -255,13 +255,14 @@ __device__ __forceinline__ void g_stream(T (&k_lds)[2][kGKt * 64],
                                          const T* ksg, const T* vsg, const GArgs<T>& A,
                                          const QFrag<T> (&qf)[CB], GCol (&st)[CB],
                                          f32x16 (&o)[CB][2], int tid, int lane) {
-  const int64_t nt = (A.m + kGKt - 1) / kGKt;
-  for (int64_t t = 0; t < nt; ++t) {
+  const int m = (int)A.m;
+  const int nt = (m + kGKt - 1) / kGKt;
+  for (int t = 0; t < nt; ++t) {
     const int b = (int)(t & 1);
     g_store<T>(stage, k_lds[b], v_lds[b], tid);
     __syncthreads();
     if (t + 1 < nt) g_load<T>(stage, ksg, vsg, (t + 1) * kGKt, A.m, tid);
-    g_tile<T, CB, MODE>(k_lds[b], v_lds[b], t * kGKt, A.m, A.c, qf, st, o, lane);
+    g_tile<T, CB, MODE>(k_lds[b], v_lds[b], t * kGKt, m, A.c, qf, st, o, lane);
   }
 }
 
@@ -281,22 +282,23 @@ __device__ __forceinline__ bf16_t* ph_buf() {
   return buf;
 }
 
-__device__ __forceinline__ void g_issue_ph(bf16_t* __restrict__ buf, int64_t ph, const bf16_t* ksg,
-                                           const bf16_t* vsg, int64_t m, int64_t nt, int tid) {
+__device__ __forceinline__ void g_issue_ph(bf16_t* __restrict__ buf, int ph, const bf16_t* ksg,
+                                           const bf16_t* vsg, int m, int nt, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   const int row = wave * 8 + (lane >> 3), pos = lane & 7;
   const int ksw = pos ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
   const int vsw = pos ^ ((2 * row) & 6);
 #pragma unroll
   for (int i = 0; i < kPhR; ++i) {
-    const int64_t t = ph * kPhR + i;
+    const int t = ph * kPhR + i;
     if (t < nt) {
-      const int64_t key = t * kGKt + row;
-      const int64_t kc = key < m ? key : m - 1;
+      const int key = t * kGKt + row;
+      const int kc = key < m ? key : m - 1;
       bf16_t* dst = buf + i * kPhTile + wave * 512;
-      __builtin_amdgcn_global_load_lds((const void*)(ksg + kc * 64 + ksw * 8), (lb::lds_ptr)dst, 16, 0,
+      const int64_t off = (int64_t)kc * 64;
+      __builtin_amdgcn_global_load_lds((const void*)(ksg + off + ksw * 8), (lb::lds_ptr)dst, 16, 0,
                                        0);
-      __builtin_amdgcn_global_load_lds((const void*)(vsg + kc * 64 + vsw * 8),
+      __builtin_amdgcn_global_load_lds((const void*)(vsg + off + vsw * 8),
                                        (lb::lds_ptr)(dst + kGKt * 64), 16, 0, 0);
     }
   }
@@ -307,21 +309,24 @@ __device__ __forceinline__ void g_stream_ph(const bf16_t* ksg, const bf16_t* vsg
                                             const GArgs<bf16_t>& A,
                                             const QFrag<bf16_t> (&qf)[CB], GCol (&st)[CB],
                                             f32x16 (&o)[CB][2], int tid, int lane) {
-  const int64_t nt = (A.m + kGKt - 1) / kGKt;
-  const int64_t nph = (nt + kPhR - 1) / kPhR;
-  auto phase = [&](int64_t ph, bf16_t* __restrict__ cur, bf16_t* __restrict__ nxt) {
+  // tile and key indices in 32 bits (M < 2^31): their compares then run on
+  // the scalar unit (gfx9 has no 64-bit scalar ordered compare)
+  const int m = (int)A.m;
+  const int nt = (m + kGKt - 1) / kGKt;
+  const int nph = (nt + kPhR - 1) / kPhR;
+  auto phase = [&](int ph, bf16_t* __restrict__ cur, bf16_t* __restrict__ nxt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (ph + 1 < nph) g_issue_ph(nxt, ph + 1, ksg, vsg, A.m, nt, tid);
+    if (ph + 1 < nph) g_issue_ph(nxt, ph + 1, ksg, vsg, m, nt, tid);
 #pragma unroll
     for (int i = 0; i < kPhR; ++i) {
-      const int64_t t = ph * kPhR + i;
+      const int t = ph * kPhR + i;
       if (t < nt)
-        g_tile<bf16_t, CB, MODE>(cur + i * kPhTile, cur + i * kPhTile + kGKt * 64, t * kGKt, A.m,
+        g_tile<bf16_t, CB, MODE>(cur + i * kPhTile, cur + i * kPhTile + kGKt * 64, t * kGKt, m,
                                  A.c, qf, st, o, lane);
     }
   };
-  for (int64_t ph = 0; ph < nph; ph += 2) {
+  for (int ph = 0; ph < nph; ph += 2) {
     phase(ph, ph_buf<0>(), ph_buf<1>());
     if (ph + 1 < nph) phase(ph + 1, ph_buf<1>(), ph_buf<0>());
   }
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
 
   GStage<T> stage;
   if constexpr (kAsync)
-    g_issue_ph(ph_buf<0>(), 0, ksg, vsg, A.m, (A.m + kGKt - 1) / kGKt, tid);
+    g_issue_ph(ph_buf<0>(), 0, ksg, vsg, (int)A.m, (int)((A.m + kGKt - 1) / kGKt), tid);
   else
     g_load<T>(stage, ksg, vsg, 0, A.m, tid);
 
