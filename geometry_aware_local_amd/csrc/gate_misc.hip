@@ -17,12 +17,8 @@ __global__ __launch_bounds__(256) void k_gate_mix(const float* __restrict__ ol,
   const int64_t row = gid >> 4;          // (token, head)
   if (row >= n * hq) return;
   const int d0 = (int)(gid & 15) * 4;
-  const int64_t tok = row / hq;
-  const float* gl = gate + (per_head ? row * 2 : tok * 2);
-  const float l0 = gl[0], l1 = gl[1];
-  const float mx = fmaxf(l0, l1);
-  const float e0 = expf(l0 - mx), e1 = expf(l1 - mx);
-  const float g0 = e0 / (e0 + e1), g1 = e1 / (e0 + e1);
+  float g0, g1;
+  gate_weights(gate, row / hq, (int)(row % hq), hq, per_head, g0, g1);
   const f32x4 a = *reinterpret_cast<const f32x4*>(ol + row * 64 + d0);
   const f32x4 b = *reinterpret_cast<const f32x4*>(oc + row * 64 + d0);
   if constexpr (std::is_same<T, float>::value) {

@@ -4,7 +4,9 @@
 // design 3: every query attends to all M block summaries; the softmax is
 // streamed (online) so no N x M score matrix exists, and only the M summary
 // vectors are materialised.  The gate (flowchart node F) mixes the result
-// with the local branch per token.
+// with the local branch per token: the local branch's kernel has already
+// written its gated share g_loc * o_loc into the output, and this kernel's
+// epilogue adds g_cmp * o_cmp to it.
 //
 // Design (gfx950):
 // * One workgroup = 8 waves = one KV group and 512 (bf16) query rows, a query
@@ -51,9 +53,8 @@ struct GArgs {
   float c;                 // multiplier of q.k~ giving log2-domain logits
   float* o_cmp;
   float* lse;
-  const float* o_loc;
   const float* gate;
-  T* out;
+  T* out;                  // gated: holds g_loc * o_loc on entry
   const float* kmax;       // [Hkv] max_j c |k~_j| (NULL: always track the max)
   int32_t gate_per_head;
   int64_t tiles;           // query tiles per KV group
@@ -439,14 +440,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
     const int64_t rbase = (tok[cb] * A.hq + head[cb]) * 64;
     if (A.lse && h == 0) A.lse[tok[cb] * A.hq + head[cb]] = (st[cb].m + __log2f(l)) * kLn2;
     float g0 = 0.0f, g1 = 0.0f;
-    if constexpr (kGate) {
-      const float* gl = A.gate + (A.gate_per_head ? (tok[cb] * A.hq + head[cb]) * 2 : tok[cb] * 2);
-      const float l0 = gl[0], l1 = gl[1];
-      const float mx = fmaxf(l0, l1);
-      const float e0 = expf(l0 - mx), e1 = expf(l1 - mx);
-      g0 = e0 / (e0 + e1);
-      g1 = e1 / (e0 + e1);
-    }
+    if constexpr (kGate) gate_weights(A.gate, tok[cb], head[cb], A.hq, A.gate_per_head, g0, g1);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -456,17 +450,18 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = o[cb][db][4 * q4 + j] * inv;
         if constexpr (kGate) {
+          // the local branch's kernel wrote its gated share g_loc * o_loc
+          // into the output; add this branch's share
           if (A.o_cmp) *reinterpret_cast<f32x4*>(A.o_cmp + rbase + d0) = r;
-          const f32x4 ol = *reinterpret_cast<const f32x4*>(A.o_loc + rbase + d0);
           if constexpr (GLds<T>::kF32) {
-            f32x4 w;
+            f32x4 w = *reinterpret_cast<const f32x4*>(A.out + rbase + d0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = g0 * ol[j] + g1 * r[j];
+            for (int j = 0; j < 4; ++j) w[j] = w[j] + g1 * r[j];
             *reinterpret_cast<f32x4*>(A.out + rbase + d0) = w;
           } else {
-            bf16x4 w;
+            bf16x4 w = *reinterpret_cast<const bf16x4*>(A.out + rbase + d0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = (bf16_t)(g0 * ol[j] + g1 * r[j]);
+            for (int j = 0; j < 4; ++j) w[j] = (bf16_t)((float)w[j] + g1 * r[j]);
             *reinterpret_cast<bf16x4*>(A.out + rbase + d0) = w;
           }
         } else {
@@ -500,7 +495,7 @@ hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, hipStream
 template <typename T, bool kGate>
 static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const void* vs,
                            int64_t m, float c, const float* kmax, float* o_cmp, float* lse,
-                           const float* o_loc, const float* gate, void* out, hipStream_t s) {
+                           const float* gate, void* out, hipStream_t s) {
   constexpr int ROWS = kGWaves * GCfg<T>::kCb * 32;
   GArgs<T> A;
   A.q = (const T*)q;
@@ -514,7 +509,6 @@ static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const v
   A.c = c;
   A.o_cmp = o_cmp;
   A.lse = lse;
-  A.o_loc = o_loc;
   A.gate = gate;
   A.out = (T*)out;
   A.kmax = kmax;
@@ -535,22 +529,21 @@ static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const v
 
 hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
                               const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
-                              float* lse, const float* o_loc, const float* gate, void* out,
-                              hipStream_t s) {
-  // gated: the epilogue mixes with the local branch and writes O (and o_cmp
-  // too when given, for the backward)
+                              float* lse, const float* gate, void* out, hipStream_t s) {
+  // gated: the epilogue adds this branch's gated share to the local branch's
+  // in out (and writes o_cmp too when given, for the backward)
   const bool gated = out != nullptr;
   // with kmax the summaries carry the softmax scale in log2 units already
   const float c = kmax ? 1.0f : g.scale * kLog2e;
   if (g.bf16)
-    return gated ? launch_g<bf16_t, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, o_loc,
-                                          gate, out, s)
-                 : launch_g<bf16_t, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse,
-                                           o_loc, gate, out, s);
-  return gated ? launch_g<float, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, o_loc,
-                                       gate, out, s)
-               : launch_g<float, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, o_loc,
-                                        gate, out, s);
+    return gated ? launch_g<bf16_t, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate,
+                                          out, s)
+                 : launch_g<bf16_t, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate,
+                                           out, s);
+  return gated ? launch_g<float, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
+                                       s)
+               : launch_g<float, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
+                                        s);
 }
 
 }  // namespace pack3d

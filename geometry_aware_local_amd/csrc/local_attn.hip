@@ -52,6 +52,9 @@ struct LArgs {
   const int32_t* c2p;
   float* o;
   float* lse;
+  const float* gate;
+  T* out;
+  int32_t gate_per_head;
   int32_t Z, Y, X, hq, hkv;
   int32_t rz, ry, rx;
   float c;                 // scale * log2(e)
@@ -246,6 +249,8 @@ __global__ __launch_bounds__(64 * LCfg<G>::W) void k_local_attn(LArgs<T> A) {
     const int head = grp * G + hh;
     const int64_t rbase = (qpos[cb] * A.hq + head) * 64;
     if (A.lse && h == 0) A.lse[qpos[cb] * A.hq + head] = (sm[cb].m + __log2f(l)) * kLn2;
+    float g0 = 0.0f, g1 = 0.0f;
+    if (A.out) gate_weights(A.gate, qpos[cb], head, A.hq, A.gate_per_head, g0, g1);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -253,21 +258,26 @@ __global__ __launch_bounds__(64 * LCfg<G>::W) void k_local_attn(LArgs<T> A) {
         f32x4 r;
 #pragma unroll
         for (int j = 0; j < 4; ++j) r[j] = o[cb][db][4 * q4 + j] * inv;
-        *reinterpret_cast<f32x4*>(A.o + rbase + db * 32 + 8 * q4 + 4 * h) = r;
+        const int64_t at = rbase + db * 32 + 8 * q4 + 4 * h;
+        if (A.o) *reinterpret_cast<f32x4*>(A.o + at) = r;
+        if (A.out) store_gated4<T>(A.out + at, r, g0);
       }
   }
 }
 
 template <typename T, int G>
 static hipError_t launch_l(const Geom& g, const void* q, const void* k, const void* v,
-                           const int32_t* c2p, float* o, float* lse, hipStream_t s) {
+                           const int32_t* c2p, const LocalOut& lo, hipStream_t s) {
   LArgs<T> A;
   A.q = (const T*)q;
   A.k = (const T*)k;
   A.v = (const T*)v;
   A.c2p = c2p;
-  A.o = o;
-  A.lse = lse;
+  A.o = lo.o_loc;
+  A.lse = lo.lse;
+  A.gate = lo.gate;
+  A.out = (T*)lo.out;
+  A.gate_per_head = g.gate_per_head;
   A.Z = g.Z;
   A.Y = g.Y;
   A.X = g.X;
@@ -288,23 +298,23 @@ static hipError_t launch_l(const Geom& g, const void* q, const void* k, const vo
 
 template <typename T>
 static hipError_t launch_lt(const Geom& g, const void* q, const void* k, const void* v,
-                            const int32_t* c2p, float* o, float* lse, hipStream_t s) {
+                            const int32_t* c2p, const LocalOut& lo, hipStream_t s) {
   switch (g.G) {
-    case 1: return launch_l<T, 1>(g, q, k, v, c2p, o, lse, s);
-    case 2: return launch_l<T, 2>(g, q, k, v, c2p, o, lse, s);
-    case 4: return launch_l<T, 4>(g, q, k, v, c2p, o, lse, s);
-    case 8: return launch_l<T, 8>(g, q, k, v, c2p, o, lse, s);
-    case 16: return launch_l<T, 16>(g, q, k, v, c2p, o, lse, s);
+    case 1: return launch_l<T, 1>(g, q, k, v, c2p, lo, s);
+    case 2: return launch_l<T, 2>(g, q, k, v, c2p, lo, s);
+    case 4: return launch_l<T, 4>(g, q, k, v, c2p, lo, s);
+    case 8: return launch_l<T, 8>(g, q, k, v, c2p, lo, s);
+    case 16: return launch_l<T, 16>(g, q, k, v, c2p, lo, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot, const void* v,
-                             const int32_t* c2p, float* o_loc, float* lse, hipStream_t s) {
+                             const int32_t* c2p, const LocalOut& lo, hipStream_t s) {
   if (g.bf16 && local_bf16_serves(g.G))
-    return launch_local_attn_bf16(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
-  if (g.bf16) return launch_lt<bf16_t>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
-  return launch_lt<float>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
+    return launch_local_attn_bf16(g, q_rot, k_rot, v, c2p, lo, s);
+  if (g.bf16) return launch_lt<bf16_t>(g, q_rot, k_rot, v, c2p, lo, s);
+  return launch_lt<float>(g, q_rot, k_rot, v, c2p, lo, s);
 }
 
 }  // namespace pack3d

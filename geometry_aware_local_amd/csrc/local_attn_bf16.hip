@@ -36,8 +36,11 @@ struct Args {
   const bf16_t* k;
   const bf16_t* v;
   const int32_t* c2p;
-  float* o;
+  float* o;                // fp32 o_loc (nullable)
   float* lse;
+  const float* gate;
+  bf16_t* out;             // gated share g_loc * o_loc (nullable)
+  int32_t gate_per_head;
   int32_t Z, Y, X, hq, hkv;
   int32_t rz, ry, rx;
   float c;                 // scale * log2(e)
@@ -258,6 +261,8 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
   const int head = grp * G + hh;
   const int64_t rbase = (qpos * A.hq + head) * 64;
   if (A.lse && h == 0) A.lse[qpos * A.hq + head] = (sm.m + __log2f(l)) * kLn2;
+  float g0 = 0.0f, g1 = 0.0f;
+  if (A.out) gate_weights(A.gate, qpos, head, A.hq, A.gate_per_head, g0, g1);
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     f32x4 r0, r1;
@@ -266,8 +271,15 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
       r0[j] = o0[4 * q4 + j] * inv;
       r1[j] = o1[4 * q4 + j] * inv;
     }
-    *reinterpret_cast<f32x4*>(A.o + rbase + 8 * q4 + 4 * h) = r0;
-    *reinterpret_cast<f32x4*>(A.o + rbase + 32 + 8 * q4 + 4 * h) = r1;
+    const int64_t a0 = rbase + 8 * q4 + 4 * h, a1 = a0 + 32;
+    if (A.o) {
+      *reinterpret_cast<f32x4*>(A.o + a0) = r0;
+      *reinterpret_cast<f32x4*>(A.o + a1) = r1;
+    }
+    if (A.out) {
+      store_gated4<bf16_t>(A.out + a0, r0, g0);
+      store_gated4<bf16_t>(A.out + a1, r1, g0);
+    }
   }
 }
 
@@ -460,6 +472,8 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
       const int head = grp * G + hh;
       const int64_t rbase = ((int64_t)qpos * A.hq + head) * 64;
       if (A.lse && h == 0) A.lse[(int64_t)qpos * A.hq + head] = (sm.m + __log2f(l)) * kLn2;
+      float g0 = 0.0f, g1 = 0.0f;
+      if (A.out) gate_weights(A.gate, qpos, head, A.hq, A.gate_per_head, g0, g1);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         f32x4 r0, r1;
@@ -468,8 +482,15 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
           r0[j] = o0[4 * q4 + j] * inv;
           r1[j] = o1[4 * q4 + j] * inv;
         }
-        *reinterpret_cast<f32x4*>(A.o + rbase + 8 * q4 + 4 * h) = r0;
-        *reinterpret_cast<f32x4*>(A.o + rbase + 32 + 8 * q4 + 4 * h) = r1;
+        const int64_t a0 = rbase + 8 * q4 + 4 * h, a1 = a0 + 32;
+        if (A.o) {
+          *reinterpret_cast<f32x4*>(A.o + a0) = r0;
+          *reinterpret_cast<f32x4*>(A.o + a1) = r1;
+        }
+        if (A.out) {
+          store_gated4<bf16_t>(A.out + a0, r0, g0);
+          store_gated4<bf16_t>(A.out + a1, r1, g0);
+        }
       }
     }
     o0 = f32x16{};
@@ -545,15 +566,18 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
 
 template <int G>
 hipError_t launch(const Geom& g, const void* q, const void* k, const void* v, const int32_t* c2p,
-                  float* o, float* lse, hipStream_t s) {
+                  const LocalOut& lo, hipStream_t s) {
   using C = Cfg<G>;
   Args A;
   A.q = (const bf16_t*)q;
   A.k = (const bf16_t*)k;
   A.v = (const bf16_t*)v;
   A.c2p = c2p;
-  A.o = o;
-  A.lse = lse;
+  A.o = lo.o_loc;
+  A.lse = lo.lse;
+  A.gate = lo.gate;
+  A.out = (bf16_t*)lo.out;
+  A.gate_per_head = g.gate_per_head;
   A.Z = g.Z;
   A.Y = g.Y;
   A.X = g.X;
@@ -593,12 +617,12 @@ hipError_t launch(const Geom& g, const void* q, const void* k, const void* v, co
 bool local_bf16_serves(int G) { return G == 4 || G == 8 || G == 16; }
 
 hipError_t launch_local_attn_bf16(const Geom& g, const void* q_rot, const void* k_rot,
-                                  const void* v, const int32_t* c2p, float* o_loc, float* lse,
+                                  const void* v, const int32_t* c2p, const LocalOut& lo,
                                   hipStream_t s) {
   switch (g.G) {
-    case 4: return lb::launch<4>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
-    case 8: return lb::launch<8>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
-    case 16: return lb::launch<16>(g, q_rot, k_rot, v, c2p, o_loc, lse, s);
+    case 4: return lb::launch<4>(g, q_rot, k_rot, v, c2p, lo, s);
+    case 8: return lb::launch<8>(g, q_rot, k_rot, v, c2p, lo, s);
+    case 16: return lb::launch<16>(g, q_rot, k_rot, v, c2p, lo, s);
     default: return hipErrorInvalidValue;
   }
 }

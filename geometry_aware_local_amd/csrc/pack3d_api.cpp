@@ -126,8 +126,11 @@ bool local_supported(const Geom& g) {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// The forward's workspace: rotated Q and K_loc, the summaries (keys pre-scaled),
+// their norms and the per-group maximum norm.  The local branch writes its
+// gated share straight into the output, so no o_loc buffer exists.
 struct WsLayout {
-  size_t q_rot, k_rot, k_sum, v_sum, o_loc, knorm, kmax, total;
+  size_t q_rot, k_rot, k_sum, v_sum, knorm, kmax, total;
 };
 
 WsLayout ws_layout(const Geom& g) {
@@ -142,8 +145,6 @@ WsLayout ws_layout(const Geom& g) {
   off += align256((size_t)g.Hkv * g.M * 64 * es);
   w.v_sum = off;
   off += align256((size_t)g.Hkv * g.M * 64 * es);
-  w.o_loc = off;
-  off += align256((size_t)g.N * g.Hq * 64 * 4);
   w.knorm = off;
   off += align256((size_t)g.Hkv * g.M * 4);
   w.kmax = off;
@@ -308,7 +309,8 @@ int pack3d_local_attn(const pack3d_problem* prob, const void* q_rot, const void*
                            {cell_to_pos, "cell_to_pos"}, {o_loc, "o_loc"}, {lse_loc, "lse_loc"}})))
     return rc;
   return hip_status(
-      launch_local_attn(g, q_rot, k_rot, v, cell_to_pos, o_loc, lse_loc, (hipStream_t)stream),
+      launch_local_attn(g, q_rot, k_rot, v, cell_to_pos, LocalOut{o_loc, lse_loc, nullptr, nullptr},
+                        (hipStream_t)stream),
       "k_local_attn");
 }
 
@@ -326,7 +328,7 @@ int pack3d_global_attn(const pack3d_problem* prob, const void* q_rot, const void
                                                  {lse_cmp, "lse_cmp"}})))
     return rc;
   return hip_status(launch_global_attn(g, q_rot, k_sum, v_sum, m, nullptr, o_cmp, lse_cmp,
-                                       nullptr, nullptr, nullptr, (hipStream_t)stream),
+                                       nullptr, nullptr, (hipStream_t)stream),
                     "k_global_attn");
 }
 
@@ -385,7 +387,6 @@ int forward_launch(const Geom& g, const FwdArgs& x, void* workspace, hipStream_t
   void* k_rot = ws + w.k_rot;
   void* k_sum = ws + w.k_sum;
   void* v_sum = ws + w.v_sum;
-  float* o_loc = (float*)(ws + w.o_loc);
   float* knorm = (float*)(ws + w.knorm);
   float* kmax = (float*)(ws + w.kmax);
   int stage = 0;
@@ -408,14 +409,14 @@ int forward_launch(const Geom& g, const FwdArgs& x, void* workspace, hipStream_t
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  if ((e = launch_local_attn(g, q_rot, k_rot, x.v_loc, x.cell_to_pos, o_loc, nullptr, s)) !=
-      hipSuccess)
+  // the local branch writes its gated share g_loc * o_loc into out
+  if ((e = launch_local_attn(g, q_rot, k_rot, x.v_loc, x.cell_to_pos,
+                             LocalOut{nullptr, nullptr, x.gate, x.out}, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   // the compressed branch's query: rotated, or the input q when it is blind
   const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? x.q : q_rot;
-  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, nullptr, nullptr, o_loc, x.gate,
-                         x.out, s);
+  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, nullptr, nullptr, x.gate, x.out, s);
   if (e != hipSuccess) return hip_status(e, "k_global_attn(gated)");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   return ok();
@@ -556,12 +557,14 @@ int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* 
                                 g.scale * 1.4426950408889634f, knorm, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
-  if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos, o_loc, lse_loc, s)) != hipSuccess)
+  // the local branch saves o_loc and writes its gated share into out, as in
+  // the inference forward
+  if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos,
+                             LocalOut{o_loc, lse_loc, gate_logits, out}, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
   const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? q : q_rot;
   // the compressed branch with the gate fused, also saving o_cmp and lse_cmp
-  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, o_loc, gate_logits,
-                         out, s);
+  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, gate_logits, out, s);
   return hip_status(e, "k_global_attn");
 }
 
@@ -653,8 +656,7 @@ int check_width(const Geom& g, int32_t width, const char* fn) {
 }
 
 struct LayerLayout {
-  size_t x, q_raw, q_rot, k_rot, v_loc, k_cmp, v_cmp, k_sum, v_sum, o_loc, knorm, kmax, o,
-      total;
+  size_t x, q_raw, q_rot, k_rot, v_loc, k_cmp, v_cmp, k_sum, v_sum, knorm, kmax, o, total;
 };
 
 LayerLayout layer_layout(const Geom& g, int32_t width) {
@@ -674,7 +676,6 @@ LayerLayout layer_layout(const Geom& g, int32_t width) {
   take(w.v_cmp, nk);
   take(w.k_sum, (size_t)g.Hkv * g.M * 64 * 2);
   take(w.v_sum, (size_t)g.Hkv * g.M * 64 * 2);
-  take(w.o_loc, (size_t)g.N * g.Hq * 64 * 4);
   take(w.knorm, (size_t)g.Hkv * g.M * 4);
   take(w.kmax, (size_t)g.Hkv * 4);
   take(w.o, nq);
@@ -758,7 +759,6 @@ int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* 
   void* q_raw = blind ? ws + w.q_raw : nullptr;
   float* knorm = (float*)(ws + w.knorm);
   float* kmax = (float*)(ws + w.kmax);
-  float* o_loc = (float*)(ws + w.o_loc);
   hipError_t e;
   if ((e = launch_layernorm(g, width, h, gamma, beta, eps, ws + w.x, s)) != hipSuccess)
     return hip_status(e, "k_layernorm");
@@ -770,11 +770,12 @@ int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* 
       hipSuccess)
     return hip_status(e, "k_block_summary");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
-  if ((e = launch_local_attn(g, ws + w.q_rot, ws + w.k_rot, ws + w.v_loc, cell_to_pos, o_loc,
-                             nullptr, s)) != hipSuccess)
+  if ((e = launch_local_attn(g, ws + w.q_rot, ws + w.k_rot, ws + w.v_loc, cell_to_pos,
+                             LocalOut{nullptr, nullptr, gate_logits, ws + w.o}, s)) !=
+      hipSuccess)
     return hip_status(e, "k_local_attn");
   e = launch_global_attn(g, blind ? q_raw : ws + w.q_rot, ws + w.k_sum, ws + w.v_sum, g.M, kmax,
-                         nullptr, nullptr, o_loc, gate_logits, ws + w.o, s);
+                         nullptr, nullptr, gate_logits, ws + w.o, s);
   if (e != hipSuccess) return hip_status(e, "k_global_attn(gated)");
   return hip_status(launch_out_proj(g, width, ws + w.o, w_o, h, out, s), "k_gemm<residual>");
 }

@@ -108,6 +108,39 @@ __device__ __forceinline__ void summary_sincos(const Geom& g, int chunk, int z, 
   }
 }
 
+// The tokenwise gate (notes, flowchart node F): a 2-way softmax over the
+// logits of token tok (or of token tok and head `head` when per_head), index
+// 0 the local branch, 1 the compressed one.  Every kernel that applies the
+// gate goes through this function, so g_loc and g_cmp have the same bits
+// wherever they are computed.
+__device__ __forceinline__ void gate_weights(const float* gate, int64_t tok, int head, int hq,
+                                             int per_head, float& g0, float& g1) {
+  const float* gl = gate + (per_head ? (tok * hq + head) * 2 : tok * 2);
+  const float l0 = gl[0], l1 = gl[1];
+  const float mx = fmaxf(l0, l1);
+  const float e0 = expf(l0 - mx), e1 = expf(l1 - mx);
+  g0 = e0 / (e0 + e1);
+  g1 = e1 / (e0 + e1);
+}
+
+// The local branch's share of the output: out[row, d0 .. d0+3] = g_loc * r,
+// rounded to the output dtype (the compressed branch's epilogue adds its
+// share to it).
+template <typename T>
+__device__ __forceinline__ void store_gated4(T* out, const f32x4& r, float g0) {
+  if constexpr (std::is_same<T, float>::value) {
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = g0 * r[j];
+    *reinterpret_cast<f32x4*>(out) = w;
+  } else {
+    bf16x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (bf16_t)(g0 * r[j]);
+    *reinterpret_cast<bf16x4*>(out) = w;
+  }
+}
+
 // Load / store 8 consecutive elements as floats.
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* v) {

@@ -48,24 +48,33 @@ hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_
                                 void* v_sum, float kscale, float* knorm, hipStream_t s);
 // kmax[g] = max over the M key-summary norms of group g.
 hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, hipStream_t s);
+// Local branch.  o_loc (nullable): fp32 [N, Hq, 64]; lse (nullable): fp32
+// [N, Hq]; out (nullable, with gate): the local branch's gated share
+// g_loc * o_loc written into the output [N, Hq, 64] in the problem dtype.
+struct LocalOut {
+  float* o_loc;
+  float* lse;
+  const float* gate;
+  void* out;
+};
 hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot,
-                             const void* v, const int32_t* cell_to_pos, float* o_loc,
-                             float* lse, hipStream_t s);
+                             const void* v, const int32_t* cell_to_pos, const LocalOut& lo,
+                             hipStream_t s);
 // The bf16 kernel with compile-time plane geometry serves these group sizes;
 // launch_local_attn dispatches to it.
 bool local_bf16_serves(int G);
 hipError_t launch_local_attn_bf16(const Geom& g, const void* q_rot, const void* k_rot,
-                                  const void* v, const int32_t* cell_to_pos, float* o_loc,
-                                  float* lse, hipStream_t s);
-// out != nullptr: gate-mix epilogue, out = g_loc*o_loc + g_cmp*o_cmp in the
-// problem dtype (o_cmp, fp32, also written when non-null).  Otherwise o_cmp
-// (fp32) only.  lse != nullptr: natural-log lse per row.  kmax != nullptr:
-// the key summaries are pre-scaled by scale*log2(e) and kmax[g] bounds their
-// norms (enables the fixed softmax reference); nullptr: unscaled summaries.
+                                  const void* v, const int32_t* cell_to_pos, const LocalOut& lo,
+                                  hipStream_t s);
+// out != nullptr: gated epilogue; out holds the local branch's gated share on
+// entry and receives out + g_cmp*o_cmp in the problem dtype (o_cmp, fp32,
+// also written when non-null).  Otherwise o_cmp (fp32) only.  lse !=
+// nullptr: natural-log lse per row.  kmax != nullptr: the key summaries are
+// pre-scaled by scale*log2(e) and kmax[g] bounds their norms (enables the
+// fixed softmax reference); nullptr: unscaled summaries.
 hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
                               const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
-                              float* lse, const float* o_loc, const float* gate, void* out,
-                              hipStream_t s);
+                              float* lse, const float* gate, void* out, hipStream_t s);
 // Backward (bf16).  Inputs, the forward's saved state, workspace buffers and
 // outputs of one backward launch sequence.
 struct BwdBuffers {

@@ -208,7 +208,7 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
  * holds until the process ends.  The call allocates nothing.
  *   - Problems whose pack3d_forward_workspace_size() exceeds that size are
  *     rejected with PACK3D_ERR_WORKSPACE before any launch (at 8 query heads,
- *     2 KV groups and bf16, up to ~78 000 tokens).
+ *     2 KV groups and bf16, 1312.5 bytes per token: up to ~204 000 tokens).
  *   - Every call on a GPU shares that GPU's array, which keeps the last
  *     call's contents (the forward writes every part it reads, so nothing
  *     needs clearing): calls that overlap on one GPU (different streams, no

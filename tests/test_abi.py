@@ -120,7 +120,9 @@ def test_workspace_size_matches_layout(pk):
     p = _prob(pk, grid=(64, 64, 64), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
     n, m = 64 ** 3, 64 ** 3 // 16
     a256 = lambda b: (b + 255) // 256 * 256
-    fp32_parts = 4 * n * 8 * 64 + a256(4 * 2 * m) + a256(4 * 2)   # o_loc, summary norms, kmax
+    # summary norms and kmax; the local branch writes its gated share into
+    # the output, so there is no fp32 o_loc section
+    fp32_parts = a256(4 * 2 * m) + a256(4 * 2)
     bf16 = 2 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) + fp32_parts
     assert pk.pack3d_forward_workspace_size(p) == bf16
     p.dtype = 0
@@ -199,15 +201,14 @@ def test_layer_entry_points_check_arguments_on_the_host(pk):
 
 
 def test_layer_workspace_layout(pk):
-    """LayerNorm(h), the five projections, summaries, o_loc, norms and the
-    gated output, each section 256-byte aligned (the unrotated Q only for
-    the coordinate-blind branch)."""
+    """LayerNorm(h), the five projections, summaries, norms and the gated
+    output, each section 256-byte aligned (the unrotated Q only for the
+    coordinate-blind branch)."""
     a256 = lambda b: (b + 255) // 256 * 256
     p = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1)
     n, m, hq, hkv = 1024, 64, 4, 1
     want = (a256(2 * n * 512) + 2 * a256(2 * n * hq * 64) + 4 * a256(2 * n * hkv * 64)
-            + 2 * a256(2 * hkv * m * 64) + a256(4 * n * hq * 64) + a256(4 * hkv * m)
-            + a256(4 * hkv))
+            + 2 * a256(2 * hkv * m * 64) + a256(4 * hkv * m) + a256(4 * hkv))
     assert pk.pack3d_layer_workspace_size(p, 512) == want
     pb = _prob(pk, dtype=torch.bfloat16, n_q_heads=4, n_kv_heads=1, summary_mode="blind")
     assert pk.pack3d_layer_workspace_size(pb, 512) == want + a256(2 * n * hq * 64)

@@ -219,9 +219,27 @@ def _check_forward(pk, w, inp, rows):
     assert gu.max_rel(gu.host(o_loc)[rows], ref["o_loc"]) <= gu.REL_TOL[w.dtype]
     assert gu.max_rel(gu.host(o_cmp)[rows], ref["o_cmp"]) <= gu.REL_TOL[w.dtype]
     _check_fused_branches(pk, prob, fargs, out, ref, rows, w.dtype)
-    # the split chain's gate gives the fused forward's result
-    mixed = pk.pack3d_gate_mix(prob, o_loc, o_cmp, d["gate"])
-    assert gu.max_abs(gu.host(mixed), gu.host(out)) <= (1e-6 if w.dtype == "f32" else 1e-2)
+    # the split chain's gate gives the fused forward's result.  Both take the
+    # same local branch; their compressed branches differ (the fused one
+    # streams summaries pre-scaled into log2 units, rounded once more), each
+    # within the per-branch bound of the oracle.  In bf16 the fused forward
+    # also passes the local branch's gated share g_loc * o_loc through the
+    # output dtype before adding the compressed share (bf16 keeps 8
+    # significant bits: <= 2^-8 |g_loc o_loc|), and each result carries its
+    # final rounding (<= 2^-8 |mix| each).
+    mixed = gu.host(pk.pack3d_gate_mix(prob, o_loc, o_cmp, d["gate"]))
+    diff = np.abs(mixed - gu.host(out))
+    cmp_bound = 2 * gu.REL_TOL[w.dtype] * float(np.abs(gu.host(o_cmp)).max())
+    if w.dtype == "f32":
+        assert diff.max() <= cmp_bound + 1e-6
+    else:
+        g = orc.gate_weights(inp.gate)
+        g_loc = g[:, None, 0:1] if g.ndim == 2 else g[..., 0:1]
+        share = np.abs(g_loc * gu.host(o_loc))
+        bound = 2.0 ** -8 * (share + 2 * np.abs(mixed)) + cmp_bound + 1e-6
+        worst = float((diff / bound).max())
+        _say(f"  split vs fused: largest difference / its bound {worst:.3f}")
+        assert worst <= 1.0
     return out, o_loc, o_cmp, ref
 
 
