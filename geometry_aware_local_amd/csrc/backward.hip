@@ -66,8 +66,8 @@ __device__ __forceinline__ void tr_frags(const bf16_t* t, int row0, int db, int 
     }
 }
 
-__device__ __forceinline__ f32x16 contract_dims(const bf16x8 (&a)[4], const QFrag<bf16_t>& b) {
-  f32x16 acc = {};
+__device__ __forceinline__ f32x16 contract_dims(const bf16x8 (&a)[4], const QFrag<bf16_t>& b,
+                                                 f32x16 acc = f32x16{}) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc = Mma<bf16_t>::mma(a[s], b.f[s], acc);
   return acc;
@@ -182,14 +182,15 @@ constexpr int kGW = 8, kGCb = 2, kGRows = kGW * kGCb * 32, kGKt = 64;
 struct GdqArgs {
   const bf16_t* q;         // rotated queries [N, Hq, 64]
   const bf16_t* dco;       // g_cmp * dO [N, Hq, 64]
-  const bf16_t* ks;        // summaries [Hkv, M, 64] (unscaled)
+  const bf16_t* ks;        // key summaries [Hkv, M, 64]
   const bf16_t* vs;
   const float* lse;        // lse_cmp [N, Hq]
   const float* dd;         // D_cmp [N, Hq]
   float* dq;               // in: local dq (tau included); out: + summary dq
   int64_t m, n;
   int32_t hq, hkv, grp;
-  float c, tau;            // c = tau * log2(e)
+  float c;                 // q . ks * c = the log2-domain logit
+  float tau;               // tau * sum dS ks = dq
   int64_t tiles;
   int32_t xcd_per;
 };
@@ -336,7 +337,7 @@ struct GkvArgs {
   float* dv;
   int64_t m, ncell;
   int32_t hq, hkv, grp;
-  float c, tau;
+  float tau;
   int64_t nkt;             // key tiles (of 256) per group
   int32_t nsplit;
   int64_t cps;             // cells per slice
@@ -400,9 +401,10 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     st16(q_l[b] + TL::chunk_off(srow, sch), sg.ok ? sg.q : z);
     st16(d_l[b] + TL::chunk_off(srow, sch), sg.ok ? sg.d : z);
-    // the row's 8 threads write the same values
-    ls_l[b][srow] = sg.ok ? sg.l * kLog2e : __builtin_inff();
-    dd_l[b][srow] = sg.ok ? sg.dd : 0.0f;
+    // the row's 8 threads write the same values: -lse (log2 units) and -D,
+    // the starting values of the S and dP accumulators
+    ls_l[b][srow] = sg.ok ? -(sg.l * kLog2e) : -__builtin_inff();
+    dd_l[b][srow] = sg.ok ? -sg.dd : 0.0f;
   };
   auto tile = [&](int b) {
 #pragma unroll
@@ -410,9 +412,10 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
       bf16x8 qr[4], dr[4];
       row_frags(q_l[b], rb * 32 + col, h, qr);
       row_frags(d_l[b], rb * 32 + col, h, dr);
-      const f32x16 s = contract_dims(qr, kq);
-      const f32x16 dp = contract_dims(dr, vq);
-      f32x16 p, ds;
+      // accumulator element v holds query row rb*32 + 8*(v/4) + 4h + v%4:
+      // start S at -lse and dP at -D, so the products come out as the
+      // exponent of p and as dP - D
+      f32x16 nl, nd;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int r0 = rb * 32 + 8 * q4 + 4 * h;
@@ -420,10 +423,17 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
         const f32x4 D = *reinterpret_cast<const f32x4*>(&dd_l[b][r0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int v = 4 * q4 + j;
-          p[v] = __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -L[j]));
-          ds[v] = p[v] * (dp[v] - D[j]);
+          nl[4 * q4 + j] = L[j];
+          nd[4 * q4 + j] = D[j];
         }
+      }
+      const f32x16 s = contract_dims(qr, kq, nl);
+      const f32x16 dp = contract_dims(dr, vq, nd);
+      f32x16 p, ds;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        p[v] = __builtin_amdgcn_exp2f(s[v]);
+        ds[v] = p[v] * dp[v];
       }
       bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -1069,8 +1079,10 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
     A.hq = g.Hq;
     A.hkv = g.Hkv;
     A.grp = g.G;
-    A.c = g.scale * kLog2e;
-    A.tau = g.scale;
+    // the summaries carry tau * log2(e): logits need no factor, and
+    // sum dS k~ takes tau / (tau log2(e)) to give dq
+    A.c = 1.0f;
+    A.tau = g.scale / logit_scale(g);
     A.tiles = (g.N * g.G + bw::kGRows - 1) / bw::kGRows;
     int64_t blocks;
     if (g.Hkv <= kNumXcd && kNumXcd % g.Hkv == 0) {
@@ -1141,7 +1153,6 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
     A.hq = g.Hq;
     A.hkv = g.Hkv;
     A.grp = g.G;
-    A.c = g.scale * kLog2e;
     A.tau = g.scale;
     A.nkt = (g.M + bw::kKKeys - 1) / bw::kKKeys;
     A.nsplit = (int32_t)nsplit;

@@ -404,7 +404,7 @@ int forward_launch(const Geom& g, const FwdArgs& x, void* workspace, hipStream_t
   // summaries scaled into log2-domain logits, with their norms for the
   // softmax bound of the query->summary kernel
   if ((e = launch_block_summary(g, x.k_cmp, x.v_cmp, x.a, x.cell_to_pos, k_sum, v_sum,
-                                g.scale * 1.4426950408889634f, knorm, s)) != hipSuccess)
+                                logit_scale(g), knorm, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
@@ -554,7 +554,7 @@ int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* 
   if ((e = launch_rope(g, k_loc, k_rot, g.Hkv, coords, s)) != hipSuccess)
     return hip_status(e, "k_rope(k_loc)");
   if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
-                                g.scale * 1.4426950408889634f, knorm, s)) != hipSuccess)
+                                logit_scale(g), knorm, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
   // the local branch saves o_loc and writes its gated share into out, as in
@@ -627,13 +627,14 @@ int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc
   b.dv_cmp = dv_cmp;
   b.dgate = dgate;
   hipError_t e;
-  // recompute the rotations and the (unscaled) summaries
+  // recompute the rotations and the summaries (keys scaled into log2-domain
+  // logits, as in the forward)
   if ((e = launch_rope(g, q, ws + w.q_rot, g.Hq, coords, s)) != hipSuccess)
     return hip_status(e, "k_rope(q)");
   if ((e = launch_rope(g, k_loc, ws + w.k_rot, g.Hkv, coords, s)) != hipSuccess)
     return hip_status(e, "k_rope(k_loc)");
-  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, ws + w.k_sum, ws + w.v_sum, 1.0f,
-                                nullptr, s)) != hipSuccess)
+  if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, ws + w.k_sum, ws + w.v_sum,
+                                logit_scale(g), nullptr, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
   return hip_status(launch_backward(g, b, s), fn);
 }
@@ -766,7 +767,7 @@ int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* 
                            ws + w.v_loc, ws + w.k_cmp, ws + w.v_cmp, s)) != hipSuccess)
     return hip_status(e, "k_gemm<qkv>");
   if ((e = launch_block_summary(g, ws + w.k_cmp, ws + w.v_cmp, a, cell_to_pos, ws + w.k_sum,
-                                ws + w.v_sum, g.scale * 1.4426950408889634f, knorm, s)) !=
+                                ws + w.v_sum, logit_scale(g), knorm, s)) !=
       hipSuccess)
     return hip_status(e, "k_block_summary");
   if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");

@@ -38,6 +38,10 @@ struct Geom {
   RopeTab rope;
 };
 
+// tau * log2(e): the factor the key summaries carry in the forward and the
+// backward, so q . k~ is a log2-domain logit.
+inline float logit_scale(const Geom& g) { return g.scale * 1.4426950408889634f; }
+
 // Launchers (each returns the launch status; no host synchronisation).
 hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
                        const int32_t* coords, hipStream_t s);
@@ -89,7 +93,7 @@ struct BwdBuffers {
   const float* lse_loc;        // saved [N, Hq]
   const float* lse_cmp;        // saved [N, Hq]
   const void* q_cmp;           // the compressed branch's query (q_rot, or q if blind)
-  const void* q_rot;           // workspace: rotated q, k_loc, unscaled summaries
+  const void* q_rot;           // workspace: rotated q, k_loc, the summaries (keys x logit_scale)
   const void* k_rot;
   const void* k_sum;
   const void* v_sum;
