@@ -1,9 +1,11 @@
 #!/usr/bin/env python
 """Benchmark of the PACK3D local-global attention forward on one MI355X.
 
-One step = one ``pack3d_forward`` over the whole synthetic workload (RoPE on
-Q and K_loc, block summaries, local attention, query->summary attention with
-the fused gate), inputs resident in HBM.  Prints ONE JSON line with the
+One step = one ``pack3d_forward`` over the whole synthetic workload (its four
+launches: the block pass building the summaries and rotating K_loc, the
+per-group summary-norm maximum with the rotary table, local attention and
+query->summary attention, each rotating Q in registers and adding its gated
+share to the output), inputs resident in HBM.  Prints ONE JSON line with the
 throughput in tokens/s, the roofline position of the dominant kernel
 (k_global_attn, bf16 MFMA), per-kernel figures, and the fp64 CPU oracle timed
 on a bounded sample of the same workload on this host's cores.  A second leg
@@ -83,10 +85,15 @@ def algorithmic(w: sg.Workload) -> dict:
     es = 2 if w.dtype == "bf16" else 4
     nbr = window_pairs(w.grid, w.window)
     return {
-        # rope: read + write Q and K_loc, read coords (twice: one launch each)
-        "rope_bytes": 2 * n * (hq + hkv) * 64 * es + 2 * n * 12,
         # summary: read K_cmp, V_cmp, a, cell_to_pos; write K~, V~
         "summary_bytes": 2 * n * hkv * 64 * es + n * hkv * 4 + n * 4 + 2 * hkv * m * 64 * es,
+        # the forward's block pass: the summaries, their norms, and K_loc read,
+        # rotated and written
+        "block_pass_bytes": (2 * n * hkv * 64 * es + n * hkv * 4 + n * 4 + 2 * hkv * m * 64 * es
+                             + hkv * m * 4 + 2 * n * hkv * 64 * es),
+        # the compressed kernel's HBM streams: Q read (unrotated) with coords,
+        # the local share read and the output written, the summaries once
+        "global_bytes": 3 * n * hq * 64 * es + n * 12 + 2 * hkv * m * 64 * es,
         # local: QK^T and PV over every clipped window
         "local_flops": 4 * nbr * hq * 64,
         # global: QK^T and PV against all M summaries: 256 flops per (row, summary)
@@ -418,10 +425,6 @@ def main() -> int:
     work = algorithmic(w)
     es = 2 if w.dtype == "bf16" else 4
     peak_mfma = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    rope_q = 2 * n * w.n_q_heads * 64 * es + n * 12
-    rope_k = 2 * n * w.n_kv_heads * 64 * es + n * 12
-    # the forward's summary stage also writes the key-summary norms
-    summary = work["summary_bytes"] + w.n_kv_heads * w.n_blocks * 4
     gbs = lambda b, t: b / (t * 1e-3) / 1e9
     tfl = lambda f, t: f / (t * 1e-3) / 1e12
     # kernel serving each stage (see pack3d_backend_info)
@@ -429,17 +432,18 @@ def main() -> int:
     local_kernel = (("k_local_zrun" if w.window[0] == 3 else "k_local_bf16") if fast_local
                     else "k_local_attn")
     kernels = {
-        "k_rope(q)": {"ms": stages["rope(q)"], "bound": "hbm",
-                      "gbs": gbs(rope_q, stages["rope(q)"])},
-        "k_rope(k_loc)": {"ms": stages["rope(k_loc)"], "bound": "hbm",
-                          "gbs": gbs(rope_k, stages["rope(k_loc)"])},
-        "k_block_summary": {"ms": stages["block_summary"], "bound": "hbm",
-                            "gbs": gbs(summary, stages["block_summary"])},
-        "k_kmax": {"ms": stages["kmax"], "bound": "launch"},
+        # one pass over the blocks: summaries with their norms + RoPE of K_loc
+        "k_block_summary(+rope k_loc)": {"ms": stages["block_pass"], "bound": "hbm",
+                                         "gbs": gbs(work["block_pass_bytes"],
+                                                    stages["block_pass"])},
+        "k_kmax(+rope table)": {"ms": stages["kmax+rope_table"], "bound": "launch"},
+        # query->summary attention, RoPE of Q and the compressed gated share
+        "k_global_attn(gated)": {"ms": stages["global_attn+gate"], "bound": "mfma",
+                                 "tflops": tfl(work["global_flops"], stages["global_attn+gate"]),
+                                 "hbm_gbs": gbs(work["global_bytes"],
+                                                stages["global_attn+gate"])},
         local_kernel: {"ms": stages["local_attn"], "bound": "mfma",
                        "tflops": tfl(work["local_flops"], stages["local_attn"])},
-        "k_global_attn(gated)": {"ms": stages["global_attn+gate"], "bound": "mfma",
-                                 "tflops": tfl(work["global_flops"], stages["global_attn+gate"])},
     }
     for v in kernels.values():
         if v["bound"] == "hbm":

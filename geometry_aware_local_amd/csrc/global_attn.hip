@@ -8,6 +8,10 @@
 // written its gated share g_loc * o_loc into the output, and this kernel's
 // epilogue adds g_cmp * o_cmp to it.
 //
+// In the forward the kernel takes the unrotated queries and rotates each
+// query fragment by R(c) (key design 1) once, in registers, through the
+// lattice's rotary table, so no rotated copy of Q is ever stored.
+//
 // Design (gfx950):
 // * One workgroup = 8 waves = one KV group and 512 (bf16) query rows, a query
 //   row being a (token, head) pair of that group: the G heads sharing the
@@ -56,6 +60,8 @@ struct GArgs {
   const float* gate;
   T* out;                  // gated: holds g_loc * o_loc on entry
   const float* kmax;       // [Hkv] max_j c |k~_j| (NULL: always track the max)
+  const int32_t* coords;   // [N, 3], with qrope.tab: q is unrotated
+  QRope qrope;
   int32_t gate_per_head;
   int64_t tiles;           // query tiles per KV group
   int32_t xcd_per;         // consecutive XCDs sharing a group (0: plain order)
@@ -383,6 +389,10 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
     tok[cb] = valid[cb] ? row / A.grp : 0;
     head[cb] = grp * A.grp + (valid[cb] ? (int)(row % A.grp) : 0);
     load_qfrag<T>(qf[cb], A.q + (tok[cb] * A.hq + head[cb]) * 64 + h * 32, valid[cb]);
+    if (A.qrope.tab) {
+      const int32_t* c3 = A.coords + 3 * tok[cb];
+      rotate_qfrag<T>(qf[cb], A.qrope, h, c3[0], c3[1], c3[2]);
+    }
     st[cb].l = 0.0f;
     st[cb].m = kNegInf;
     st[cb].track = true;
@@ -453,17 +463,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
           // the local branch's kernel wrote its gated share g_loc * o_loc
           // into the output; add this branch's share
           if (A.o_cmp) *reinterpret_cast<f32x4*>(A.o_cmp + rbase + d0) = r;
-          if constexpr (GLds<T>::kF32) {
-            f32x4 w = *reinterpret_cast<const f32x4*>(A.out + rbase + d0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = w[j] + g1 * r[j];
-            *reinterpret_cast<f32x4*>(A.out + rbase + d0) = w;
-          } else {
-            bf16x4 w = *reinterpret_cast<const bf16x4*>(A.out + rbase + d0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w[j] = (bf16_t)((float)w[j] + g1 * r[j]);
-            *reinterpret_cast<bf16x4*>(A.out + rbase + d0) = w;
-          }
+          add_gated4<T>(A.out + rbase + d0, r, g1);
         } else {
           *reinterpret_cast<f32x4*>(A.o_cmp + rbase + d0) = r;
         }
@@ -471,9 +471,22 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   }
 }
 
-// kmax[g] = max_j part[g][j] over nparts per-block summary norms.
+// kmax[g] = max_j part[g][j] over nparts per-block summary norms (blocks
+// 0 .. Hkv-1).  The blocks after them fill the lattice's rotary table, one
+// (pair, coordinate) entry per thread, with k_rope's sines and cosines.
 __global__ __launch_bounds__(1024) void k_kmax(const float* __restrict__ part, int64_t nparts,
-                                               float* kmax) {
+                                               int32_t groups, float* kmax, float* tab, int32_t ts,
+                                               RopeTab rt) {
+  if ((int)blockIdx.x >= groups) {
+    const int e = ((int)blockIdx.x - groups) * 1024 + (int)threadIdx.x;
+    if (e >= kMaxPairs * ts) return;
+    const int p = e / ts, c = e % ts;
+    float sn = 0.0f, cs = 1.0f;
+    if (p < rt.npairs) rope_sincos(rt.nu[p], (double)c, sn, cs);
+    tab[2 * e] = sn;
+    tab[2 * e + 1] = cs;
+    return;
+  }
   __shared__ float red[1024];
   const float* p = part + (int64_t)blockIdx.x * nparts;
   float x = 0.0f;
@@ -487,15 +500,19 @@ __global__ __launch_bounds__(1024) void k_kmax(const float* __restrict__ part, i
   if (threadIdx.x == 0) kmax[blockIdx.x] = red[0];
 }
 
-hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, hipStream_t s) {
-  hipLaunchKernelGGL(k_kmax, dim3(g.Hkv), dim3(1024), 0, s, knorm, (int64_t)g.M, kmax);
+hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, float* tab, hipStream_t s) {
+  const int ts = rope_table_stride(g);
+  const int extra = tab ? (kMaxPairs * ts + 1023) / 1024 : 0;
+  hipLaunchKernelGGL(k_kmax, dim3(g.Hkv + extra), dim3(1024), 0, s, knorm, (int64_t)g.M, g.Hkv,
+                     kmax, tab, ts, g.rope);
   return hipGetLastError();
 }
 
 template <typename T, bool kGate>
 static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const void* vs,
                            int64_t m, float c, const float* kmax, float* o_cmp, float* lse,
-                           const float* gate, void* out, hipStream_t s) {
+                           const float* gate, void* out, const int32_t* coords,
+                           const QRope& qr, hipStream_t s) {
   constexpr int ROWS = kGWaves * GCfg<T>::kCb * 32;
   GArgs<T> A;
   A.q = (const T*)q;
@@ -513,6 +530,8 @@ static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const v
   A.out = (T*)out;
   A.kmax = kmax;
   A.gate_per_head = g.gate_per_head;
+  A.coords = coords;
+  A.qrope = qr;
   A.tiles = (g.N * g.G + ROWS - 1) / ROWS;
   int64_t blocks;
   if (g.Hkv <= kNumXcd && kNumXcd % g.Hkv == 0) {
@@ -527,23 +546,24 @@ static hipError_t launch_g(const Geom& g, const void* q, const void* ks, const v
   return hipGetLastError();
 }
 
-hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
-                              const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
-                              float* lse, const float* gate, void* out, hipStream_t s) {
+hipError_t launch_global_attn(const Geom& g, const void* q, const void* k_sum, const void* v_sum,
+                              int64_t m, const float* kmax, float* o_cmp, float* lse,
+                              const float* gate, void* out, const int32_t* coords,
+                              const QRope& qr, hipStream_t s) {
   // gated: the epilogue adds this branch's gated share to the local branch's
   // in out (and writes o_cmp too when given, for the backward)
   const bool gated = out != nullptr;
   // with kmax the summaries carry the softmax scale in log2 units already
   const float c = kmax ? 1.0f : g.scale * kLog2e;
   if (g.bf16)
-    return gated ? launch_g<bf16_t, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate,
-                                          out, s)
-                 : launch_g<bf16_t, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate,
-                                           out, s);
-  return gated ? launch_g<float, true>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
-                                       s)
-               : launch_g<float, false>(g, q_rot, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
-                                        s);
+    return gated ? launch_g<bf16_t, true>(g, q, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
+                                          coords, qr, s)
+                 : launch_g<bf16_t, false>(g, q, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
+                                           coords, qr, s);
+  return gated ? launch_g<float, true>(g, q, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
+                                       coords, qr, s)
+               : launch_g<float, false>(g, q, k_sum, v_sum, m, c, kmax, o_cmp, lse, gate, out,
+                                        coords, qr, s);
 }
 
 }  // namespace pack3d

@@ -46,7 +46,8 @@ struct LCfg {
 
 template <typename T>
 struct LArgs {
-  const T* q;
+  const T* q;              // rotated, or unrotated with qrope.tab
+  QRope qrope;
   const T* k;
   const T* v;
   const int32_t* c2p;
@@ -106,6 +107,7 @@ __global__ __launch_bounds__(64 * LCfg<G>::W) void k_local_attn(LArgs<T> A) {
     const bool ok = yq < A.Y && xq < A.X;
     qpos[cb] = ok ? (int64_t)A.c2p[((int64_t)z0 * A.Y + yq) * A.X + xq] : -1;
     load_qfrag<T>(qf[cb], A.q + (qpos[cb] * A.hq + grp * G + hh) * 64 + h * 32, ok);
+    if (A.qrope.tab) rotate_qfrag<T>(qf[cb], A.qrope, h, z0, ok ? yq : 0, ok ? xq : 0);
     // window and lattice mask of each (key block, accumulator element)
 #pragma unroll
     for (int w = 0; w < C::MWORDS; ++w) mbits[cb][w] = 0;
@@ -267,9 +269,11 @@ __global__ __launch_bounds__(64 * LCfg<G>::W) void k_local_attn(LArgs<T> A) {
 
 template <typename T, int G>
 static hipError_t launch_l(const Geom& g, const void* q, const void* k, const void* v,
-                           const int32_t* c2p, const LocalOut& lo, hipStream_t s) {
+                           const int32_t* c2p, const LocalOut& lo, const QRope& qr,
+                           hipStream_t s) {
   LArgs<T> A;
   A.q = (const T*)q;
+  A.qrope = qr;
   A.k = (const T*)k;
   A.v = (const T*)v;
   A.c2p = c2p;
@@ -298,23 +302,25 @@ static hipError_t launch_l(const Geom& g, const void* q, const void* k, const vo
 
 template <typename T>
 static hipError_t launch_lt(const Geom& g, const void* q, const void* k, const void* v,
-                            const int32_t* c2p, const LocalOut& lo, hipStream_t s) {
+                            const int32_t* c2p, const LocalOut& lo, const QRope& qr,
+                            hipStream_t s) {
   switch (g.G) {
-    case 1: return launch_l<T, 1>(g, q, k, v, c2p, lo, s);
-    case 2: return launch_l<T, 2>(g, q, k, v, c2p, lo, s);
-    case 4: return launch_l<T, 4>(g, q, k, v, c2p, lo, s);
-    case 8: return launch_l<T, 8>(g, q, k, v, c2p, lo, s);
-    case 16: return launch_l<T, 16>(g, q, k, v, c2p, lo, s);
+    case 1: return launch_l<T, 1>(g, q, k, v, c2p, lo, qr, s);
+    case 2: return launch_l<T, 2>(g, q, k, v, c2p, lo, qr, s);
+    case 4: return launch_l<T, 4>(g, q, k, v, c2p, lo, qr, s);
+    case 8: return launch_l<T, 8>(g, q, k, v, c2p, lo, qr, s);
+    case 16: return launch_l<T, 16>(g, q, k, v, c2p, lo, qr, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot, const void* v,
-                             const int32_t* c2p, const LocalOut& lo, hipStream_t s) {
+hipError_t launch_local_attn(const Geom& g, const void* q, const void* k_rot, const void* v,
+                             const int32_t* c2p, const LocalOut& lo, const QRope& qr,
+                             hipStream_t s) {
   if (g.bf16 && local_bf16_serves(g.G))
-    return launch_local_attn_bf16(g, q_rot, k_rot, v, c2p, lo, s);
-  if (g.bf16) return launch_lt<bf16_t>(g, q_rot, k_rot, v, c2p, lo, s);
-  return launch_lt<float>(g, q_rot, k_rot, v, c2p, lo, s);
+    return launch_local_attn_bf16(g, q, k_rot, v, c2p, lo, qr, s);
+  if (g.bf16) return launch_lt<bf16_t>(g, q, k_rot, v, c2p, lo, qr, s);
+  return launch_lt<float>(g, q, k_rot, v, c2p, lo, qr, s);
 }
 
 }  // namespace pack3d

@@ -32,7 +32,8 @@ namespace pack3d {
 namespace lb {
 
 struct Args {
-  const bf16_t* q;
+  const bf16_t* q;         // rotated, or unrotated with qrope.tab
+  QRope qrope;
   const bf16_t* k;
   const bf16_t* v;
   const int32_t* c2p;
@@ -116,6 +117,9 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
   const int64_t qpos = qok ? (int64_t)A.c2p[((int64_t)z0 * A.Y + yq) * A.X + xq] : -1;
   QFrag<bf16_t> qf;
   load_qfrag<bf16_t>(qf, A.q + (qpos * A.hq + grp * G + hh) * 64 + h * 32, qok);
+  // unrotated query: rotate it here (lanes past the lattice hold zeros and
+  // read the table at a cell inside it)
+  if (A.qrope.tab) rotate_qfrag<bf16_t>(qf, A.qrope, h, z0, qok ? yq : 0, qok ? xq : 0);
 
   // Window mask.  Key slot s of the patch is region cell (py0 + s/8, px0 +
   // s%8); accumulator element e of 32-key block kb on lane half h is slot
@@ -294,7 +298,8 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
 // overlap three planes of compute.  The planes are visited in the same order
 // as in k_local_bf16, so the results are the same bit for bit.
 // ---------------------------------------------------------------------------
-template <int G>
+// kRot: the query is unrotated; its fragments are rotated through A.qrope.
+template <int G, bool kRot>
 __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
   using C = Cfg<G>;
   constexpr int PY = C::PY, PX = C::PX, TX = C::TX, NKB = C::NKB, KY = C::KY, RX = C::RX,
@@ -363,6 +368,8 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
   // this lane's query column: (yq, xq) of every plane of the run
   const int yq = y0 + py0 + qy, xq = x0 + px0 + qx;
   const bool qok = yq < A.Y && xq < A.X;
+  const int yc = qok ? yq : 0, xc = qok ? xq : 0;     // in-lattice table coordinates
+  const uint32_t rab = qrope_lane_axes(A.qrope, h);
   const uint32_t qcell = qok ? (uint32_t)(yq * A.X + xq) : 0u;
   const uint32_t plane_cells = (uint32_t)(A.Y * A.X);
   const bf16_t* qg = A.q + (int64_t)(grp * G + hh) * 64 + h * 32;
@@ -526,6 +533,7 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
   int32_t qpos_n = A.c2p[(uint32_t)(zs + 1 < A.Z ? zs + 1 : zs) * plane_cells + qcell];
   __builtin_amdgcn_s_waitcnt(0);
   load_qfrag<bf16_t>(qf, qrow(qpos), qok);
+  if constexpr (kRot) rotate_qfrag<bf16_t>(qf, A.qrope, h, zs, yc, xc);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -546,6 +554,24 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
     // the copies of plane z0 + 1 have landed; every wave is done with slot R
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // unrotated queries: rotate the next plane's fragments (landed at the
+    // barrier) before this step's plane copies are issued, so waiting for
+    // the table reads never waits for the copies (a plane past the lattice
+    // reads the last one's (sin, cos), unused)
+    if constexpr (kRot) {
+      QRopeCS rcs;
+      qrope_load(rcs, A.qrope, rab, h, z0 + 1 < A.Z ? z0 + 1 : z0, yc, xc);
+      qrope_apply<bf16_t>(qf_n, rcs);
+      // keep the rotation (and its wait) ahead of the copies: an empty asm
+      // that takes the rotated fragments pins their computation here
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 w = __builtin_bit_cast(u32x4, qf_n.f[q]);
+        asm volatile("" : "+v"(w));
+        qf_n.f[q] = __builtin_bit_cast(bf16x8, w);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (z0 + 2 < A.Z && z0 + 1 < ze) issue_loads(pos_n, ka, va);
     if (z0 + 3 < A.Z && z0 + 2 < ze) load_pos(z0 + 3, pos_n);
     compute_plane(qf, kb_, vb);
@@ -566,10 +592,11 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
 
 template <int G>
 hipError_t launch(const Geom& g, const void* q, const void* k, const void* v, const int32_t* c2p,
-                  const LocalOut& lo, hipStream_t s) {
+                  const LocalOut& lo, const QRope& qr, hipStream_t s) {
   using C = Cfg<G>;
   Args A;
   A.q = (const bf16_t*)q;
+  A.qrope = qr;
   A.k = (const bf16_t*)k;
   A.v = (const bf16_t*)v;
   A.c2p = c2p;
@@ -600,8 +627,12 @@ hipError_t launch(const Geom& g, const void* q, const void* k, const void* v, co
     nruns = (g.Z + A.zrun - 1) / A.zrun;
     A.nblocks = cols * nruns;
     A.per_xcd = (A.nblocks + kNumXcd - 1) / kNumXcd;
-    hipLaunchKernelGGL(k_local_zrun<G>, dim3((unsigned)(A.per_xcd * kNumXcd)), dim3(64 * C::W),
-                       0, s, A);
+    if (qr.tab)
+      hipLaunchKernelGGL((k_local_zrun<G, true>), dim3((unsigned)(A.per_xcd * kNumXcd)),
+                         dim3(64 * C::W), 0, s, A);
+    else
+      hipLaunchKernelGGL((k_local_zrun<G, false>), dim3((unsigned)(A.per_xcd * kNumXcd)),
+                         dim3(64 * C::W), 0, s, A);
     return hipGetLastError();
   }
   A.zrun = 1;
@@ -616,13 +647,13 @@ hipError_t launch(const Geom& g, const void* q, const void* k, const void* v, co
 
 bool local_bf16_serves(int G) { return G == 4 || G == 8 || G == 16; }
 
-hipError_t launch_local_attn_bf16(const Geom& g, const void* q_rot, const void* k_rot,
+hipError_t launch_local_attn_bf16(const Geom& g, const void* q, const void* k_rot,
                                   const void* v, const int32_t* c2p, const LocalOut& lo,
-                                  hipStream_t s) {
+                                  const QRope& qr, hipStream_t s) {
   switch (g.G) {
-    case 4: return lb::launch<4>(g, q_rot, k_rot, v, c2p, lo, s);
-    case 8: return lb::launch<8>(g, q_rot, k_rot, v, c2p, lo, s);
-    case 16: return lb::launch<16>(g, q_rot, k_rot, v, c2p, lo, s);
+    case 4: return lb::launch<4>(g, q, k_rot, v, c2p, lo, qr, s);
+    case 8: return lb::launch<8>(g, q, k_rot, v, c2p, lo, qr, s);
+    case 16: return lb::launch<16>(g, q, k_rot, v, c2p, lo, qr, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -126,19 +126,21 @@ bool local_supported(const Geom& g) {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// The forward's workspace: rotated Q and K_loc, the summaries (keys pre-scaled),
-// their norms and the per-group maximum norm.  The local branch writes its
-// gated share straight into the output, so no o_loc buffer exists.
+// The forward's workspace: the lattice's rotary table, rotated K_loc, the
+// summaries (keys pre-scaled), their norms and the per-group maximum norm.
+// Both attention kernels rotate Q in registers, so no rotated Q is stored,
+// and the local branch writes its gated share straight into the output, so
+// no o_loc buffer exists.
 struct WsLayout {
-  size_t q_rot, k_rot, k_sum, v_sum, knorm, kmax, total;
+  size_t tab, k_rot, k_sum, v_sum, knorm, kmax, total;
 };
 
 WsLayout ws_layout(const Geom& g) {
   const size_t es = g.bf16 ? 2 : 4;
   WsLayout w;
   size_t off = 0;
-  w.q_rot = off;
-  off += align256((size_t)g.N * g.Hq * 64 * es);
+  w.tab = off;
+  off += align256(rope_table_bytes(g));
   w.k_rot = off;
   off += align256((size_t)g.N * g.Hkv * 64 * es);
   w.k_sum = off;
@@ -290,7 +292,7 @@ int pack3d_block_summary(const pack3d_problem* prob, const void* k_cmp, const vo
                            {cell_to_pos, "cell_to_pos"}, {k_sum, "k_sum"}, {v_sum, "v_sum"}})))
     return rc;
   return hip_status(launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum, 1.0f,
-                                         nullptr, (hipStream_t)stream),
+                                         nullptr, nullptr, nullptr, (hipStream_t)stream),
                     "k_block_summary");
 }
 
@@ -310,6 +312,7 @@ int pack3d_local_attn(const pack3d_problem* prob, const void* q_rot, const void*
     return rc;
   return hip_status(
       launch_local_attn(g, q_rot, k_rot, v, cell_to_pos, LocalOut{o_loc, lse_loc, nullptr, nullptr},
+                        no_qrope(),
                         (hipStream_t)stream),
       "k_local_attn");
 }
@@ -328,7 +331,8 @@ int pack3d_global_attn(const pack3d_problem* prob, const void* q_rot, const void
                                                  {lse_cmp, "lse_cmp"}})))
     return rc;
   return hip_status(launch_global_attn(g, q_rot, k_sum, v_sum, m, nullptr, o_cmp, lse_cmp,
-                                       nullptr, nullptr, (hipStream_t)stream),
+                                       nullptr, nullptr, nullptr, no_qrope(),
+                                       (hipStream_t)stream),
                     "k_global_attn");
 }
 
@@ -383,7 +387,7 @@ int forward_launch(const Geom& g, const FwdArgs& x, void* workspace, hipStream_t
                    void* const* ev) {
   const WsLayout w = ws_layout(g);
   char* ws = (char*)workspace;
-  void* q_rot = ws + w.q_rot;
+  float* tab = (float*)(ws + w.tab);
   void* k_rot = ws + w.k_rot;
   void* k_sum = ws + w.k_sum;
   void* v_sum = ws + w.v_sum;
@@ -395,28 +399,28 @@ int forward_launch(const Geom& g, const FwdArgs& x, void* workspace, hipStream_t
   };
   hipError_t e;
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  if ((e = launch_rope(g, x.q, q_rot, g.Hq, x.coords, s)) != hipSuccess)
-    return hip_status(e, "k_rope(q)");
-  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  if ((e = launch_rope(g, x.k_loc, k_rot, g.Hkv, x.coords, s)) != hipSuccess)
-    return hip_status(e, "k_rope(k_loc)");
-  if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  // summaries scaled into log2-domain logits, with their norms for the
-  // softmax bound of the query->summary kernel
+  // one pass over the blocks: summaries scaled into log2-domain logits, with
+  // their norms for the softmax bound of the query->summary kernel, and the
+  // rotated K_loc
   if ((e = launch_block_summary(g, x.k_cmp, x.v_cmp, x.a, x.cell_to_pos, k_sum, v_sum,
-                                logit_scale(g), knorm, s)) != hipSuccess)
+                                logit_scale(g), knorm, x.k_loc, k_rot, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
+  // the per-group norm bound, and the rotary table both attention kernels
+  // rotate Q through
+  if ((e = launch_kmax(g, knorm, kmax, tab, s)) != hipSuccess) return hip_status(e, "k_kmax");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
+  const QRope qr = make_qrope(g, tab);
   // the local branch writes its gated share g_loc * o_loc into out
-  if ((e = launch_local_attn(g, q_rot, k_rot, x.v_loc, x.cell_to_pos,
-                             LocalOut{nullptr, nullptr, x.gate, x.out}, s)) != hipSuccess)
+  if ((e = launch_local_attn(g, x.q, k_rot, x.v_loc, x.cell_to_pos,
+                             LocalOut{nullptr, nullptr, x.gate, x.out}, qr, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
-  // the compressed branch's query: rotated, or the input q when it is blind
-  const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? x.q : q_rot;
-  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, nullptr, nullptr, x.gate, x.out, s);
+  // the compressed branch adds g_cmp * o_cmp; its query is rotated, or the
+  // input q as given when the branch is blind
+  const bool blind = g.summary_mode == PACK3D_SUMMARY_BLIND;
+  e = launch_global_attn(g, x.q, k_sum, v_sum, g.M, kmax, nullptr, nullptr, x.gate, x.out,
+                         x.coords, blind ? no_qrope() : qr, s);
   if (e != hipSuccess) return hip_status(e, "k_global_attn(gated)");
   if ((e = mark()) != hipSuccess) return hip_status(e, "hipEventRecord");
   return ok();
@@ -539,7 +543,7 @@ int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   char* sv = (char*)saved;
-  void* q_rot = ws + w.q_rot;
+  float* tab = (float*)(ws + w.tab);
   void* k_rot = ws + w.k_rot;
   void* k_sum = ws + w.k_sum;
   void* v_sum = ws + w.v_sum;
@@ -550,21 +554,19 @@ int pack3d_forward_train(const pack3d_problem* prob, const void* q, const void* 
   float* lse_loc = (float*)(sv + sl.lse_loc);
   float* lse_cmp = (float*)(sv + sl.lse_cmp);
   hipError_t e;
-  if ((e = launch_rope(g, q, q_rot, g.Hq, coords, s)) != hipSuccess) return hip_status(e, "k_rope(q)");
-  if ((e = launch_rope(g, k_loc, k_rot, g.Hkv, coords, s)) != hipSuccess)
-    return hip_status(e, "k_rope(k_loc)");
   if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, k_sum, v_sum,
-                                logit_scale(g), knorm, s)) != hipSuccess)
+                                logit_scale(g), knorm, k_loc, k_rot, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
-  if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
-  // the local branch saves o_loc and writes its gated share into out, as in
-  // the inference forward
-  if ((e = launch_local_attn(g, q_rot, k_rot, v_loc, cell_to_pos,
-                             LocalOut{o_loc, lse_loc, gate_logits, out}, s)) != hipSuccess)
+  if ((e = launch_kmax(g, knorm, kmax, tab, s)) != hipSuccess) return hip_status(e, "k_kmax");
+  // the kernels of the inference forward, also saving each branch's output
+  // and lse
+  const QRope qr = make_qrope(g, tab);
+  if ((e = launch_local_attn(g, q, k_rot, v_loc, cell_to_pos,
+                             LocalOut{o_loc, lse_loc, gate_logits, out}, qr, s)) != hipSuccess)
     return hip_status(e, "k_local_attn");
-  const void* q_cmp = g.summary_mode == PACK3D_SUMMARY_BLIND ? q : q_rot;
-  // the compressed branch with the gate fused, also saving o_cmp and lse_cmp
-  e = launch_global_attn(g, q_cmp, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, gate_logits, out, s);
+  const bool blind = g.summary_mode == PACK3D_SUMMARY_BLIND;
+  e = launch_global_attn(g, q, k_sum, v_sum, g.M, kmax, o_cmp, lse_cmp, gate_logits, out, coords,
+                         blind ? no_qrope() : qr, s);
   return hip_status(e, "k_global_attn");
 }
 
@@ -631,10 +633,8 @@ int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc
   // logits, as in the forward)
   if ((e = launch_rope(g, q, ws + w.q_rot, g.Hq, coords, s)) != hipSuccess)
     return hip_status(e, "k_rope(q)");
-  if ((e = launch_rope(g, k_loc, ws + w.k_rot, g.Hkv, coords, s)) != hipSuccess)
-    return hip_status(e, "k_rope(k_loc)");
   if ((e = launch_block_summary(g, k_cmp, v_cmp, a, cell_to_pos, ws + w.k_sum, ws + w.v_sum,
-                                logit_scale(g), nullptr, s)) != hipSuccess)
+                                logit_scale(g), nullptr, k_loc, ws + w.k_rot, s)) != hipSuccess)
     return hip_status(e, "k_block_summary");
   return hip_status(launch_backward(g, b, s), fn);
 }
@@ -767,16 +767,17 @@ int pack3d_layer_forward(const pack3d_problem* prob, int32_t width, const void* 
                            ws + w.v_loc, ws + w.k_cmp, ws + w.v_cmp, s)) != hipSuccess)
     return hip_status(e, "k_gemm<qkv>");
   if ((e = launch_block_summary(g, ws + w.k_cmp, ws + w.v_cmp, a, cell_to_pos, ws + w.k_sum,
-                                ws + w.v_sum, logit_scale(g), knorm, s)) !=
+                                ws + w.v_sum, logit_scale(g), knorm, nullptr, nullptr, s)) !=
       hipSuccess)
     return hip_status(e, "k_block_summary");
-  if ((e = launch_kmax(g, knorm, kmax, s)) != hipSuccess) return hip_status(e, "k_kmax");
+  if ((e = launch_kmax(g, knorm, kmax, nullptr, s)) != hipSuccess) return hip_status(e, "k_kmax");
+  // the projection's epilogue rotated Q and K_loc already
   if ((e = launch_local_attn(g, ws + w.q_rot, ws + w.k_rot, ws + w.v_loc, cell_to_pos,
-                             LocalOut{nullptr, nullptr, gate_logits, ws + w.o}, s)) !=
+                             LocalOut{nullptr, nullptr, gate_logits, ws + w.o}, no_qrope(), s)) !=
       hipSuccess)
     return hip_status(e, "k_local_attn");
   e = launch_global_attn(g, blind ? q_raw : ws + w.q_rot, ws + w.k_sum, ws + w.v_sum, g.M, kmax,
-                         nullptr, nullptr, gate_logits, ws + w.o, s);
+                         nullptr, nullptr, gate_logits, ws + w.o, nullptr, no_qrope(), s);
   if (e != hipSuccess) return hip_status(e, "k_global_attn(gated)");
   return hip_status(launch_out_proj(g, width, ws + w.o, w_o, h, out, s), "k_gemm<residual>");
 }

@@ -61,12 +61,14 @@ __device__ __forceinline__ void rope_sincos(double nu, double c, float& sn, floa
 }
 
 // Rotate 4 consecutive pairs (dims 8*chunk .. 8*chunk+7) held as floats.
+// The fused multiply-adds are written out, so every kernel that rotates a
+// row (whatever the compiler would contract) produces the same bits.
 __device__ __forceinline__ void rotate8(float* v, const float* sn, const float* cs) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float x0 = v[2 * i], x1 = v[2 * i + 1];
-    v[2 * i] = cs[i] * x0 - sn[i] * x1;
-    v[2 * i + 1] = sn[i] * x0 + cs[i] * x1;
+    v[2 * i] = fmaf(cs[i], x0, -(sn[i] * x1));
+    v[2 * i + 1] = fmaf(sn[i], x0, cs[i] * x1);
   }
 }
 
@@ -123,9 +125,9 @@ __device__ __forceinline__ void gate_weights(const float* gate, int64_t tok, int
   g1 = e1 / (e0 + e1);
 }
 
-// The local branch's share of the output: out[row, d0 .. d0+3] = g_loc * r,
+// The local branch's share of the output: out[row, d0 .. d0+3] = g * r,
 // rounded to the output dtype (the compressed branch's epilogue adds its
-// share to it).
+// share to it with add_gated4).
 template <typename T>
 __device__ __forceinline__ void store_gated4(T* out, const f32x4& r, float g0) {
   if constexpr (std::is_same<T, float>::value) {
@@ -137,6 +139,22 @@ __device__ __forceinline__ void store_gated4(T* out, const f32x4& r, float g0) {
     bf16x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = (bf16_t)(g0 * r[j]);
+    *reinterpret_cast<bf16x4*>(out) = w;
+  }
+}
+
+// out[row, d0 .. d0+3] += g * r, rounded once to the output dtype.
+template <typename T>
+__device__ __forceinline__ void add_gated4(T* out, const f32x4& r, float g) {
+  if constexpr (std::is_same<T, float>::value) {
+    f32x4 w = *reinterpret_cast<const f32x4*>(out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = w[j] + g * r[j];
+    *reinterpret_cast<f32x4*>(out) = w;
+  } else {
+    bf16x4 w = *reinterpret_cast<const bf16x4*>(out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (bf16_t)((float)w[j] + g * r[j]);
     *reinterpret_cast<bf16x4*>(out) = w;
   }
 }
@@ -258,6 +276,64 @@ __device__ __forceinline__ void load_qfrag(QFrag<T>& q, const T* row_h /* row + 
       q.f[s] = v;
     }
   }
+}
+
+// The query fragment rotated by R(z, y, x) (notes, key design 1) and rounded
+// to its dtype.  The lane's dims h*32 .. h*32+31 are rotary pairs 16h .. 16h+15;
+// each pair's (sin, cos) at its axis' coordinate comes from the lattice's
+// rotary table (k_rope's values), and rotate8 is k_rope's arithmetic, so the
+// bits equal the rows k_rope writes.  (z, y, x) must lie in the lattice.
+// qrope_load and qrope_apply split the table reads from the arithmetic, so a
+// kernel can issue the reads early.
+struct QRopeCS {
+  float sn[16], cs[16];
+};
+// The axes of the lane's 16 pairs (2 bits each).  The two words are read as
+// scalars, so selecting one is a register select, not a per-lane load from
+// the kernel arguments (whose wait would also wait for every copy in flight).
+__device__ __forceinline__ uint32_t qrope_lane_axes(const QRope& r, int h) {
+  const uint32_t a0 = __builtin_amdgcn_readfirstlane(r.axes[0]);
+  const uint32_t a1 = __builtin_amdgcn_readfirstlane(r.axes[1]);
+  return h ? a1 : a0;
+}
+__device__ __forceinline__ void qrope_load(QRopeCS& t, const QRope& r, uint32_t ab, int h, int z,
+                                           int y, int x) {
+  const float* tab = r.tab + (size_t)(16 * h) * r.ts * 2;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t ax = (ab >> (2 * k)) & 3u;
+    const int c = ax == 0 ? z : (ax == 1 ? y : x);
+    const float* e = tab + ((size_t)k * r.ts + c) * 2;
+    t.sn[k] = e[0];
+    t.cs[k] = e[1];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void qrope_apply(QFrag<T>& q, const QRopeCS& t) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float v[8];
+    if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = q.f[8 * s + e];
+      rotate8(v, t.sn + 4 * s, t.cs + 4 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q.f[8 * s + e] = v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (float)q.f[s][e];
+      rotate8(v, t.sn + 4 * s, t.cs + 4 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q.f[s][e] = (bf16_t)v[e];
+    }
+  }
+}
+template <typename T>
+__device__ __forceinline__ void rotate_qfrag(QFrag<T>& q, const QRope& r, int h, int z, int y,
+                                             int x) {
+  QRopeCS t;
+  qrope_load(t, r, qrope_lane_axes(r, h), h, z, y, x);
+  qrope_apply<T>(q, t);
 }
 
 // ---------------------------------------------------------------------------

@@ -46,12 +46,39 @@ inline float logit_scale(const Geom& g) { return g.scale * 1.4426950408889634f; 
 hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
                        const int32_t* coords, hipStream_t s);
 // kscale multiplies the key summaries; knorm (nullable) receives their norms
-// [Hkv, M] after scaling.
+// [Hkv, M] after scaling.  k_loc / k_rot (nullable): the same pass also
+// writes k_rot = R(c) k_loc [N, Hkv, 64], the rows k_rope would write.
 hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_cmp,
                                 const float* a, const int32_t* cell_to_pos, void* k_sum,
-                                void* v_sum, float kscale, float* knorm, hipStream_t s);
-// kmax[g] = max over the M key-summary norms of group g.
-hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, hipStream_t s);
+                                void* v_sum, float kscale, float* knorm, const void* k_loc,
+                                void* k_rot, hipStream_t s);
+// The lattice's rotary table: entry p * ts + c holds (sin, cos) of pair p at
+// coordinate c along the pair's axis (the identity for pairs past npairs),
+// ts = max(Z, Y, X) -- the values k_rope computes for that pair and
+// coordinate, so a rotation through the table has k_rope's bits.
+inline int32_t rope_table_stride(const Geom& g) {
+  return g.Z > g.Y ? (g.Z > g.X ? g.Z : g.X) : (g.Y > g.X ? g.Y : g.X);
+}
+inline size_t rope_table_bytes(const Geom& g) {
+  return (size_t)kMaxPairs * rope_table_stride(g) * 2 * sizeof(float);
+}
+// A kernel's view of the table: tab == nullptr means the query it gets is
+// used as given (already rotated, or unrotated for the blind branch).
+struct QRope {
+  const float* tab;        // [kMaxPairs * ts] (sin, cos) pairs
+  int32_t ts;
+  uint32_t axes[2];        // axis of pair p: bits 2(p % 16) .. +1 of axes[p / 16]
+};
+inline QRope no_qrope() { return QRope{nullptr, 0, {0u, 0u}}; }
+inline QRope make_qrope(const Geom& g, const float* tab) {
+  QRope r{tab, rope_table_stride(g), {0u, 0u}};
+  for (int p = 0; p < kMaxPairs; ++p)
+    r.axes[p / 16] |= (uint32_t)(p < g.rope.npairs ? g.rope.axis[p] : 0) << (2 * (p % 16));
+  return r;
+}
+// kmax[g] = max over the M key-summary norms of group g; tab (nullable)
+// receives the rotary table in the same launch.
+hipError_t launch_kmax(const Geom& g, const float* knorm, float* kmax, float* tab, hipStream_t s);
 // Local branch.  o_loc (nullable): fp32 [N, Hq, 64]; lse (nullable): fp32
 // [N, Hq]; out (nullable, with gate): the local branch's gated share
 // g_loc * o_loc written into the output [N, Hq, 64] in the problem dtype.
@@ -61,24 +88,29 @@ struct LocalOut {
   const float* gate;
   void* out;
 };
-hipError_t launch_local_attn(const Geom& g, const void* q_rot, const void* k_rot,
-                             const void* v, const int32_t* cell_to_pos, const LocalOut& lo,
+// qr.tab != nullptr: q is unrotated and the kernel rotates its query
+// fragments through the table; otherwise q is the rotated query.
+hipError_t launch_local_attn(const Geom& g, const void* q, const void* k_rot, const void* v,
+                             const int32_t* cell_to_pos, const LocalOut& lo, const QRope& qr,
                              hipStream_t s);
 // The bf16 kernel with compile-time plane geometry serves these group sizes;
 // launch_local_attn dispatches to it.
 bool local_bf16_serves(int G);
-hipError_t launch_local_attn_bf16(const Geom& g, const void* q_rot, const void* k_rot,
+hipError_t launch_local_attn_bf16(const Geom& g, const void* q, const void* k_rot,
                                   const void* v, const int32_t* cell_to_pos, const LocalOut& lo,
-                                  hipStream_t s);
+                                  const QRope& qr, hipStream_t s);
 // out != nullptr: gated epilogue; out holds the local branch's gated share on
 // entry and receives out + g_cmp*o_cmp in the problem dtype (o_cmp, fp32,
 // also written when non-null).  Otherwise o_cmp (fp32) only.  lse !=
 // nullptr: natural-log lse per row.  kmax != nullptr: the key summaries are
 // pre-scaled by scale*log2(e) and kmax[g] bounds their norms (enables the
-// fixed softmax reference); nullptr: unscaled summaries.
-hipError_t launch_global_attn(const Geom& g, const void* q_rot, const void* k_sum,
-                              const void* v_sum, int64_t m, const float* kmax, float* o_cmp,
-                              float* lse, const float* gate, void* out, hipStream_t s);
+// fixed softmax reference); nullptr: unscaled summaries.  qr.tab != nullptr:
+// q is unrotated and each row is rotated by R(coords[token]) through the
+// table once, in registers.
+hipError_t launch_global_attn(const Geom& g, const void* q, const void* k_sum, const void* v_sum,
+                              int64_t m, const float* kmax, float* o_cmp, float* lse,
+                              const float* gate, void* out, const int32_t* coords,
+                              const QRope& qr, hipStream_t s);
 // Backward (bf16).  Inputs, the forward's saved state, workspace buffers and
 // outputs of one backward launch sequence.
 struct BwdBuffers {

@@ -61,6 +61,11 @@ hipError_t launch_rope(const Geom& g, const void* x, void* y, int32_t heads,
 // tree, so the summation order depends only on cell positions.  The
 // summary-centre variant rotates the reduced sum once at the block centre
 // instead; the coordinate-blind variant does not rotate.
+//
+// In the forward the same pass also rotates the local branch's keys: every
+// token lies in exactly one block, so rotating K_loc of the block's cells
+// with the cells' sines and cosines (already at hand) covers the lattice and
+// writes the rows k_rope would write, in one HBM pre-pass instead of two.
 // ---------------------------------------------------------------------------
 constexpr int kSumWaves = 4;
 
@@ -69,11 +74,12 @@ constexpr int kSumWaves = 4;
 // norm of every scaled key summary in knorm [Hkv, M].
 // P = passes of 8 cells (block volume <= 8 P), fixed at compile time so the
 // per-cell rotations of small blocks take few registers.
+// kl / kr (nullable): K_loc in, R(c) K_loc out, both [N, Hkv, 64].
 template <typename T, int P>
 __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
     const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ a,
     const int32_t* __restrict__ c2p, T* __restrict__ ks, T* __restrict__ vs, Geom g,
-    float kscale, float* __restrict__ knorm) {
+    float kscale, float* __restrict__ knorm, const T* __restrict__ kl, T* __restrict__ kr) {
   const int lane = threadIdx.x & 63;
   const int64_t j = (int64_t)blockIdx.x * kSumWaves + (threadIdx.x >> 6);
   if (j >= g.M) return;
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
   const int jx = (int)(j % nbx), jy = (int)((j / nbx) % nby), jz = (int)(j / ((int64_t)nbx * nby));
   const float uniform = 1.0f / (float)g.bvol;
   const bool per_cell = g.summary_mode == PACK3D_SUMMARY_TOKEN;
+  const bool cell_rot = per_cell || kl != nullptr;
 
   // positions and rotations of the lane's cells (one per pass)
   int64_t pos[P];
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
       const int ux = u % g.bx, uy = (u / g.bx) % g.by, uz = u / (g.bx * g.by);
       const int z = jz * g.bz + uz, y = jy * g.by + uy, x = jx * g.bx + ux;
       pos[p] = c2p[((int64_t)z * g.Y + y) * g.X + x];
-      if (per_cell) chunk_sincos(g.rope, chunk, z, y, x, sn[p], cs[p]);
+      if (cell_rot) chunk_sincos(g.rope, chunk, z, y, x, sn[p], cs[p]);
     }
   }
 
@@ -109,6 +116,12 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
         float kv[8], vv[8];
         load8<T>(kc + row, kv);
         load8<T>(vc + row, vv);
+        if (kl) {
+          float lv[8];
+          load8<T>(kl + row, lv);
+          rotate8(lv, sn[p], cs[p]);
+          store8<T>(kr + row, lv);
+        }
         const float w = a ? a[pos[p] * g.Hkv + grp] : uniform;
         if (per_cell) rotate8(kv, sn[p], cs[p]);
 #pragma unroll
@@ -153,12 +166,12 @@ __global__ __launch_bounds__(64 * kSumWaves) void k_block_summary(
 template <typename T>
 static void launch_sum_t(const Geom& g, const void* k_cmp, const void* v_cmp, const float* a,
                          const int32_t* c2p, void* k_sum, void* v_sum, float kscale,
-                         float* knorm, hipStream_t s) {
+                         float* knorm, const void* k_loc, void* k_rot, hipStream_t s) {
   const dim3 grid((unsigned)((g.M + kSumWaves - 1) / kSumWaves));
   const dim3 block(64 * kSumWaves);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, (const T*)k_cmp, (const T*)v_cmp, a, c2p,
-                       (T*)k_sum, (T*)v_sum, g, kscale, knorm);
+                       (T*)k_sum, (T*)v_sum, g, kscale, knorm, (const T*)k_loc, (T*)k_rot);
   };
   static_assert(kMaxBlockVol <= 64, "block volume");
   if (g.bvol <= 8) go(k_block_summary<T, 1>);
@@ -169,11 +182,12 @@ static void launch_sum_t(const Geom& g, const void* k_cmp, const void* v_cmp, co
 
 hipError_t launch_block_summary(const Geom& g, const void* k_cmp, const void* v_cmp,
                                 const float* a, const int32_t* c2p, void* k_sum, void* v_sum,
-                                float kscale, float* knorm, hipStream_t s) {
+                                float kscale, float* knorm, const void* k_loc, void* k_rot,
+                                hipStream_t s) {
   if (g.bf16)
-    launch_sum_t<bf16_t>(g, k_cmp, v_cmp, a, c2p, k_sum, v_sum, kscale, knorm, s);
+    launch_sum_t<bf16_t>(g, k_cmp, v_cmp, a, c2p, k_sum, v_sum, kscale, knorm, k_loc, k_rot, s);
   else
-    launch_sum_t<float>(g, k_cmp, v_cmp, a, c2p, k_sum, v_sum, kscale, knorm, s);
+    launch_sum_t<float>(g, k_cmp, v_cmp, a, c2p, k_sum, v_sum, kscale, knorm, k_loc, k_rot, s);
   return hipGetLastError();
 }
 

@@ -30,9 +30,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpack3d.s
 
 PACK3D_F32, PACK3D_BF16 = 0, 1
 SUMMARY_MODES = ("token", "centre", "blind")      # pack3d_summary_mode 0, 1, 2
-PACK3D_FORWARD_STAGES = 6
-FORWARD_STAGE_NAMES = ("rope(q)", "rope(k_loc)", "block_summary", "kmax", "local_attn",
-                       "global_attn+gate")
+PACK3D_FORWARD_STAGES = 4
+FORWARD_STAGE_NAMES = ("block_pass", "kmax+rope_table", "local_attn", "global_attn+gate")
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_SHAPE", -3: "ERR_UNSUPPORTED", -4: "ERR_WORKSPACE",
           -5: "ERR_PACKING", -6: "ERR_HIP"}
 

@@ -183,15 +183,24 @@ int pack3d_gate_mix(const pack3d_problem* prob, const float* o_loc, const float*
                     const float* gate_logits, void* out, void* stream);
 
 /*
- * The whole forward in the flowchart's order (notes, overall framework):
- * RoPE on Q and K_loc, block summaries of (K_cmp, V_cmp), local attention,
- * query->summary attention with the gate fused into its epilogue.
+ * The whole forward (notes, overall framework and flowchart): RoPE on Q and
+ * K_loc, block summaries of (K_cmp, V_cmp), local attention, query->summary
+ * attention and the gate, in four launches on `stream`:
+ *   1. one pass over the blocks: the summaries (keys scaled into log2-domain
+ *      logits) with their norms, and R(c) K_loc for every token;
+ *   2. the per-group maximum summary norm, and the lattice's rotary
+ *      (sin, cos) table;
+ *   3. local attention, rotating its query fragments in registers through
+ *      the table; writes the gated share g_loc * o_loc to out;
+ *   4. query->summary attention, rotating its query fragments likewise;
+ *      adds g_cmp * o_cmp to out.
  * q: dtype [N, Hq, 64]; k_loc, v_loc, k_cmp, v_cmp: dtype [N, Hkv, 64], all
  * unrotated.  a: fp32 [N, Hkv] or NULL; coords: int32 [N, 3]; cell_to_pos:
- * int32 [N]; gate_logits: fp32 [N, 2] or [N, Hq, 2]; out: dtype [N, Hq, 64].
- * workspace: device memory of at least pack3d_forward_workspace_size() bytes,
- * 256-byte aligned, caller-owned; it holds the rotated Q/K, the summaries and
- * the fp32 local branch between the launches.
+ * int32 [N]; gate_logits: fp32 [N, 2] or [N, Hq, 2]; out: dtype [N, Hq, 64]
+ * (its prior contents are overwritten).  workspace: device memory of at
+ * least pack3d_forward_workspace_size() bytes, 256-byte aligned,
+ * caller-owned; it holds the rotary table, the rotated K_loc, the summaries
+ * and their norms between the launches.
  */
 int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
                    const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
@@ -208,7 +217,8 @@ int pack3d_forward(const pack3d_problem* prob, const void* q, const void* k_loc,
  * holds until the process ends.  The call allocates nothing.
  *   - Problems whose pack3d_forward_workspace_size() exceeds that size are
  *     rejected with PACK3D_ERR_WORKSPACE before any launch (at 8 query heads,
- *     2 KV groups and bf16, 1312.5 bytes per token: up to ~204 000 tokens).
+ *     2 KV groups and bf16, about 288.5 bytes per token: up to ~930 000
+ *     tokens).
  *   - Every call on a GPU shares that GPU's array, which keeps the last
  *     call's contents (the forward writes every part it reads, so nothing
  *     needs clearing): calls that overlap on one GPU (different streams, no
@@ -225,15 +235,16 @@ int pack3d_forward_noalloc(const pack3d_problem* prob, const void* q, const void
 /*
  * pack3d_forward with per-stage timing: the same launches, plus an event
  * recorded on `stream` before the first stage and after each of the
- * PACK3D_FORWARD_STAGES stages, in this order:
- *   0 RoPE of q, 1 RoPE of k_loc, 2 block summaries (keys pre-scaled into
- *   log2-domain logits, with their norms), 3 per-group max summary norm,
- *   4 local attention, 5 query->summary attention with the gate.
+ * PACK3D_FORWARD_STAGES stages, in this order (pack3d_forward's launches):
+ *   0 block pass (summaries, their norms, RoPE of k_loc), 1 per-group max
+ *   summary norm and the rotary table, 2 local attention (with RoPE of q,
+ *   writing its gated share), 3 query->summary attention (with RoPE of q,
+ *   adding its gated share).
  * events: PACK3D_FORWARD_STAGES + 1 hipEvent_t handles created by the caller
  * (timing enabled); n_events must equal that count.  The elapsed time
  * between events i and i+1 is stage i.  Errors as pack3d_forward.
  */
-#define PACK3D_FORWARD_STAGES 6
+#define PACK3D_FORWARD_STAGES 4
 int pack3d_forward_timed(const pack3d_problem* prob, const void* q, const void* k_loc,
                          const void* v_loc, const void* k_cmp, const void* v_cmp, const float* a,
                          const int32_t* coords, const int32_t* cell_to_pos,

@@ -120,13 +120,16 @@ def test_workspace_size_matches_layout(pk):
     p = _prob(pk, grid=(64, 64, 64), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
     n, m = 64 ** 3, 64 ** 3 // 16
     a256 = lambda b: (b + 255) // 256 * 256
-    # summary norms and kmax; the local branch writes its gated share into
-    # the output, so there is no fp32 o_loc section
+    # the rotary table (32 pairs x max extent x (sin, cos) fp32), then rotated
+    # K_loc, the summaries, their norms and kmax.  Both attention kernels
+    # rotate Q in registers (no rotated-Q section) and the local branch
+    # writes its gated share into the output (no fp32 o_loc section).
+    table = a256(32 * 64 * 2 * 4)
     fp32_parts = a256(4 * 2 * m) + a256(4 * 2)
-    bf16 = 2 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) + fp32_parts
+    bf16 = table + 2 * (n * 2 * 64 + 2 * 2 * m * 64) + fp32_parts
     assert pk.pack3d_forward_workspace_size(p) == bf16
     p.dtype = 0
-    assert pk.pack3d_forward_workspace_size(p) == 4 * (n * 8 * 64 + n * 2 * 64 + 2 * 2 * m * 64) \
+    assert pk.pack3d_forward_workspace_size(p) == table + 4 * (n * 2 * 64 + 2 * 2 * m * 64) \
         + fp32_parts
 
 
@@ -257,7 +260,7 @@ def test_noalloc_forward_checks_on_the_host(pk):
     device is touched."""
     L = pk.LIB
     small = _prob(pk, n_q_heads=8, n_kv_heads=2)
-    big = _prob(pk, grid=(64, 64, 64), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
+    big = _prob(pk, grid=(64, 128, 128), n_q_heads=8, n_kv_heads=2, window=(3, 7, 7))
     assert pk.pack3d_forward_workspace_size(small) <= pk.NOALLOC_SCRATCH_BYTES
     assert pk.pack3d_forward_workspace_size(big) > pk.NOALLOC_SCRATCH_BYTES
     fwd = [FAKE] * 10

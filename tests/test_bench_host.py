@@ -46,8 +46,11 @@ def test_headline_counts():
     assert a["global_flops"] == 4 * 262144 * 8 * 16384 * 64          # 8.80 TFLOP
     assert abs(a["global_flops"] / 8.80e12 - 1) < 1e-3
     assert a["global_bwd_flops"] == 10 * 262144 * 8 * 16384 * 64
-    # RoPE streams read and write Q and K_loc once each (bf16)
-    assert a["rope_bytes"] == 2 * 262144 * 10 * 64 * 2 + 2 * 262144 * 12
+    # the block pass: K_cmp, V_cmp read; a, cell_to_pos read; K~, V~ and the
+    # key norms written; K_loc read, rotated and written (bf16)
+    n, hkv, m = 262144, 2, 16384
+    assert a["block_pass_bytes"] == (2 * n * hkv * 64 * 2 + n * hkv * 4 + n * 4
+                                     + 2 * hkv * m * 64 * 2 + hkv * m * 4 + 2 * n * hkv * 64 * 2)
 
 
 def test_more_than_one_gpu_is_refused():
@@ -64,9 +67,10 @@ def test_committed_counters_belong_to_the_committed_kernel():
     describe another kernel (bench.py then reports null)."""
     t = bench.measured_traffic()
     assert t is not None, "profiles/ holds counters of a different k_global_attn source"
-    # at least the algorithmic bytes: Q read, summaries, o_loc read, O written
+    # at least the algorithmic bytes: Q read, rotated Q and the gated share
+    # written (bf16)
     w = sg.WORKLOADS["block_bf16_64x64x64"]
     n, hq = w.n_tokens, w.n_q_heads
-    floor = n * hq * 64 * 2 + n * hq * 64 * 4 + n * hq * 64 * 2
+    floor = 3 * n * hq * 64 * 2
     assert floor < t < 4 * floor
     assert np.isfinite(t)

@@ -220,13 +220,14 @@ def _check_forward(pk, w, inp, rows):
     assert gu.max_rel(gu.host(o_cmp)[rows], ref["o_cmp"]) <= gu.REL_TOL[w.dtype]
     _check_fused_branches(pk, prob, fargs, out, ref, rows, w.dtype)
     # the split chain's gate gives the fused forward's result.  Both take the
-    # same local branch; their compressed branches differ (the fused one
-    # streams summaries pre-scaled into log2 units, rounded once more), each
-    # within the per-branch bound of the oracle.  In bf16 the fused forward
-    # also passes the local branch's gated share g_loc * o_loc through the
-    # output dtype before adding the compressed share (bf16 keeps 8
-    # significant bits: <= 2^-8 |g_loc o_loc|), and each result carries its
-    # final rounding (<= 2^-8 |mix| each).
+    # same local branch (the fused forward rotates Q with k_rope's bits:
+    # test_fused_rotations_are_k_rope_bitwise); their compressed branches
+    # differ (the fused one streams summaries pre-scaled into log2 units,
+    # rounded once more), each within the per-branch bound of the oracle.
+    # In bf16 the fused forward also passes the local branch's gated share
+    # g_loc * o_loc through the output dtype before adding the compressed
+    # share (bf16 keeps 8 significant bits: <= 2^-8 |g_loc o_loc|), and each
+    # result carries its final rounding (<= 2^-8 |mix| each).
     mixed = gu.host(pk.pack3d_gate_mix(prob, o_loc, o_cmp, d["gate"]))
     diff = np.abs(mixed - gu.host(out))
     cmp_bound = 2 * gu.REL_TOL[w.dtype] * float(np.abs(gu.host(o_cmp)).max())
@@ -241,6 +242,38 @@ def _check_forward(pk, w, inp, rows):
         _say(f"  split vs fused: largest difference / its bound {worst:.3f}")
         assert worst <= 1.0
     return out, o_loc, o_cmp, ref
+
+
+@pytest.mark.parametrize("w", [SMALL[1], SMALL[2], SMALL[3], SMALL[12], SMALL[14],
+                               MORTON.with_(grid=(4, 32, 32))],
+                         ids=lambda w: w.name)
+def test_fused_rotations_are_k_rope_bitwise(pk, w):
+    """The forward rotates K_loc inside the block pass and Q inside both
+    attention kernels (through the rotary table).  The rotated K_loc it
+    leaves in the workspace (the section after the table) is what
+    pack3d_rope writes, bit for bit; and the training forward's local branch,
+    which rotates Q in registers, equals pack3d_local_attn fed pack3d_rope's
+    rotated Q, bit for bit (same kernel, same operands)."""
+    _say("fused rotations", w.name)
+    inp = sg.make_inputs(w)
+    d = gu.device_inputs(inp)
+    prob = gu.problem(pk, w)
+    fargs = (prob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], d["a"], d["coords"],
+             d["cell_to_pos"], d["gate"])
+    ws = pk.alloc_workspace(prob, d["q"].device)
+    ws.fill_(0xFF)
+    pk.pack3d_forward(*fargs, workspace=ws)
+    q_rot = pk.pack3d_rope(prob, d["q"], d["coords"])
+    k_rot = pk.pack3d_rope(prob, d["k_loc"], d["coords"])
+    torch.cuda.synchronize()
+    nk = k_rot.numel() * k_rot.element_size()
+    ts = max(w.grid)
+    k_off = (32 * ts * 8 + 255) // 256 * 256
+    assert torch.equal(ws[k_off:k_off + nk], k_rot.view(torch.uint8).reshape(-1))
+    _, saved = pk.pack3d_forward_train(*fargs)
+    o_loc = pk.pack3d_local_attn(prob, q_rot, k_rot, d["v_loc"], d["cell_to_pos"])
+    torch.cuda.synchronize()
+    assert torch.equal(pk.saved_views(prob, saved)["o_loc"], o_loc)
 
 
 @pytest.mark.parametrize("w", SMALL, ids=IDS)

@@ -37,7 +37,7 @@ def _both(pk, w):
 
 
 def test_noalloc_forward_matches_forward_on_consecutive_calls(pk):
-    big = W["morton_bf16_16x64x64"]                       # 65 536 tokens, ~220 MB of scratch
+    big = W["block_bf16_64x64x64"]                        # 262 144 tokens, ~76 MB of scratch
     small = big.with_(grid=(4, 16, 24), packing="random")  # 1 536 tokens, reuses the array
     tiny = W["tiny_f32_4x16x16"]                           # fp32, another layout of it
     for w in (big, small, tiny, big):
@@ -49,7 +49,7 @@ def test_noalloc_forward_matches_forward_on_consecutive_calls(pk):
 
 
 def test_noalloc_rejects_problems_beyond_the_scratch_array(pk):
-    w = W["block_bf16_64x64x64"]
+    w = W["random_bf16_64x128x128"]                      # 1 048 576 tokens, ~302 MB
     prob = gu.problem(pk, w)
     assert pk.pack3d_forward_workspace_size(prob) > pk.NOALLOC_SCRATCH_BYTES
     n = w.n_tokens
