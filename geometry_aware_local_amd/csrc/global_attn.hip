@@ -170,16 +170,34 @@ __device__ __forceinline__ void v_frags(typename Mma<T>::frag* f, const T* vl, i
 // Per-column softmax state.
 struct GCol {
   float m;       // reference (log2 units)
-  float l;       // this lane's partial sum
+  float l;       // fp32: this lane's partial sum
+  f32x4 lm;      // bf16: the column's sum, accumulated on the matrix cores
   bool track;    // true: lazily tracked running max; false: fixed reference
 };
+
+// bf16 row sums on the matrix cores.  The P fragment of a PV step (lane l
+// holds P[col = l % 32][keys 8(l/32) .. +7] of 16 keys) taken as the B
+// operand of a 16x16x32 MFMA is B[k = 8(l/16) + e][n = l % 16] =
+// P[16((l/16) % 2) + n][8((l/16)/2) + e]; with A[m][8g + e] = 1 exactly when
+// g % 2 == (m/4) % 2, D[m][n] sums the 16 keys of column 16((m/4) % 2) + n,
+// and lane l's accumulator rows m = 4(l/16) .. +3 are its own column's sum.
+// The sum thus costs one small MFMA per 16 keys instead of four v_dot2 per
+// lane, which on this part do not overlap the other wave's MFMAs.
+__device__ __forceinline__ bf16x8 rowsum_ones(int lane) {
+  const int g = lane >> 4, m = lane & 15;
+  const bf16_t v = ((g & 1) == ((m >> 2) & 1)) ? (bf16_t)1.0f : (bf16_t)0.0f;
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = v;
+  return a;
+}
 
 // One 64-key tile for all of the wave's column blocks.
 template <typename T, int CB, int MODE>
 __device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __restrict__ vl,
                                        int k0, int m,
                                        float c, const QFrag<T> (&qf)[CB], GCol (&st)[CB],
-                                       f32x16 (&o)[CB][2], int lane) {
+                                       f32x16 (&o)[CB][2], int lane, const bf16x8& ones) {
   const int h = lane >> 5, col = lane & 31;
   f32x16 s[2][CB];
 #pragma unroll
@@ -217,6 +235,7 @@ __device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __rest
         const float alpha = upd ? __builtin_amdgcn_exp2f(st[cb].m - mn) : 1.0f;
         st[cb].m = mn;
         st[cb].l *= alpha;
+        st[cb].lm *= alpha;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           o[cb][0][v] *= alpha;
@@ -238,7 +257,11 @@ __device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __rest
 #pragma unroll
       for (int t = 0; t < Mma<T>::kPvSteps; ++t) {
         pf[kb][cb][t] = Mma<T>::p_frag(p, t);
-        st[cb].l = frag_sum(pf[kb][cb][t], st[cb].l);
+        if constexpr (GLds<T>::kF32)
+          st[cb].l = frag_sum(pf[kb][cb][t], st[cb].l);
+        else
+          st[cb].lm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[kb][cb][t], st[cb].lm,
+                                                              0, 0, 0);
       }
     }
   }
@@ -269,7 +292,7 @@ __device__ __forceinline__ void g_stream(T (&k_lds)[2][kGKt * 64],
     g_store<T>(stage, k_lds[b], v_lds[b], tid);
     __syncthreads();
     if (t + 1 < nt) g_load<T>(stage, ksg, vsg, (t + 1) * kGKt, A.m, tid);
-    g_tile<T, CB, MODE>(k_lds[b], v_lds[b], t * kGKt, m, A.c, qf, st, o, lane);
+    g_tile<T, CB, MODE>(k_lds[b], v_lds[b], t * kGKt, m, A.c, qf, st, o, lane, bf16x8{});
   }
 }
 
@@ -321,6 +344,7 @@ __device__ __forceinline__ void g_stream_ph(const bf16_t* ksg, const bf16_t* vsg
   const int m = (int)A.m;
   const int nt = (m + kGKt - 1) / kGKt;
   const int nph = (nt + kPhR - 1) / kPhR;
+  const bf16x8 ones = rowsum_ones(lane);
   auto phase = [&](int ph, bf16_t* __restrict__ cur, bf16_t* __restrict__ nxt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -330,7 +354,7 @@ __device__ __forceinline__ void g_stream_ph(const bf16_t* ksg, const bf16_t* vsg
       const int t = ph * kPhR + i;
       if (t < nt)
         g_tile<bf16_t, CB, MODE>(cur + i * kPhTile, cur + i * kPhTile + kGKt * 64, t * kGKt, m,
-                                 A.c, qf, st, o, lane);
+                                 A.c, qf, st, o, lane, ones);
     }
   };
   for (int ph = 0; ph < nph; ph += 2) {
@@ -394,6 +418,7 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
       rotate_qfrag<T>(qf[cb], A.qrope, h, c3[0], c3[1], c3[2]);
     }
     st[cb].l = 0.0f;
+    st[cb].lm = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     st[cb].m = kNegInf;
     st[cb].track = true;
     if (A.kmax) {
@@ -444,7 +469,8 @@ __global__ __launch_bounds__(64 * kGWaves) void k_global_attn(GArgs<T> A) {
   // epilogue: normalise, write o_cmp or the gated output
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const float l = pair_sum(st[cb].l);
+    // bf16: the matrix cores summed both lane halves already
+    const float l = GLds<T>::kF32 ? pair_sum(st[cb].l) : st[cb].lm[0];
     if (!valid[cb]) continue;
     const float inv = 1.0f / l;
     const int64_t rbase = (tok[cb] * A.hq + head[cb]) * 64;
