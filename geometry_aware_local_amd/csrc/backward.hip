@@ -84,7 +84,9 @@ __device__ __forceinline__ f32x4 acc4(const f32x16& a, int q4, float s) {
 
 // ---------------------------------------------------------------------------
 // k_bwd_prep: one wave per token.  Lane = 16-byte chunk (8 dims) of one
-// head's row; the 8 lanes of a head reduce with XOR shuffles.
+// head's row; the 8 lanes of a head reduce with XOR shuffles.  The
+// compressed branch's D is stored negated, next to -lse * log2(e): the
+// starting values of its kernels' accumulators.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void softmax2(float l0, float l1, float& g0, float& g1) {
   const float mx = fmaxf(l0, l1);
@@ -96,9 +98,10 @@ __device__ __forceinline__ void softmax2(float l0, float l1, float& g0, float& g
 __global__ __launch_bounds__(256) void k_bwd_prep(const bf16_t* __restrict__ dout,
                                                   const float* __restrict__ o_loc,
                                                   const float* __restrict__ o_cmp,
-                                                  const float* __restrict__ gate, int64_t n,
+                                                  const float* __restrict__ gate,
+                                                  const float* __restrict__ lse_c, int64_t n,
                                                   int32_t hq, int32_t per_head, bf16_t* dlo,
-                                                  bf16_t* dco, float* dl, float* dc,
+                                                  bf16_t* dco, float* dl, float* dc, float* nls,
                                                   float* dgate) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -146,7 +149,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const bf16_t* __restrict__ dou
     }
     if (ok && (lane & 7) == 0) {
       dl[t * hq + head] = sl;
-      dc[t * hq + head] = sc;
+      dc[t * hq + head] = -sc;
+      nls[t * hq + head] = -(lse_c[t * hq + head] * kLog2e);
       if (per_head) {
         // two-logit softmax Jacobian: d l0 = g0 g1 (dg0 - dg1) = -d l1
         const float d0 = gl * gc * (pl - pc);
@@ -185,7 +189,7 @@ struct GdqArgs {
   const bf16_t* ks;        // key summaries [Hkv, M, 64]
   const bf16_t* vs;
   const float* lse;        // lse_cmp [N, Hq]
-  const float* dd;         // D_cmp [N, Hq]
+  const float* ndd;        // -D_cmp [N, Hq]
   float* dq;               // in: local dq (tau included); out: + summary dq
   int64_t m, n;
   int32_t hq, hkv, grp;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
   int64_t tok[kGCb];
   int head[kGCb];
   bool valid[kGCb];
-  float lse2[kGCb], ddv[kGCb];
+  float lse2[kGCb], nddv[kGCb];
 #pragma unroll
   for (int cb = 0; cb < kGCb; ++cb) {
     const int64_t row = tile * kGRows + (int64_t)(wave * kGCb + cb) * 32 + col;
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
     load_qfrag<bf16_t>(qf[cb], A.q + r * 64 + h * 32, valid[cb]);
     load_qfrag<bf16_t>(df[cb], A.dco + r * 64 + h * 32, valid[cb]);
     lse2[cb] = valid[cb] ? A.lse[r] * kLog2e : 0.0f;
-    ddv[cb] = valid[cb] ? A.dd[r] : 0.0f;
+    nddv[cb] = valid[cb] ? A.ndd[r] : 0.0f;
   }
   f32x16 acc[kGCb][2];
 #pragma unroll
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
         if (full) {
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            ds[v] = __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -lse2[cb])) * (dp[v] - ddv[cb]);
+            ds[v] = __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -lse2[cb])) * (dp[v] + nddv[cb]);
         } else {
           // keys past M: p = 0
           const int lim = (int)(A.m - t * kGKt) - kb * 32 - 4 * h;
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
           for (int v = 0; v < 16; ++v) {
             const bool ok = 8 * (v >> 2) + (v & 3) < lim;
             const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[v], A.c, -lse2[cb])) : 0.0f;
-            ds[v] = p * (dp[v] - ddv[cb]);
+            ds[v] = p * (dp[v] + nddv[cb]);
           }
         }
         dsf[cb][0] = Mma<bf16_t>::p_frag(ds, 0);
@@ -321,17 +325,23 @@ __global__ __launch_bounds__(64 * kGW) void k_glob_dq(GdqArgs A) {
 // k_glob_dkv: workgroup = 8 waves = 256 summaries of one group (32 per wave,
 // held in registers as MFMA B operands) x one slice of the group's query
 // stream.  The stream runs over lattice cells in raster order, 64 query rows
-// (64/G cells x G heads) per tile, gathered through cell_to_pos.
+// (64/G cells x G heads) per tile, gathered through cell_to_pos.  Tiles are
+// copied global -> LDS asynchronously in phases of kKPh tiles (rows, their
+// lse and -D): the copies of the next phase are issued at the start of a
+// phase and land while its tiles are computed; one wait + barrier per phase
+// publishes them and frees the previous phase's buffer.
 // ---------------------------------------------------------------------------
 constexpr int kKW = 8, kKKeys = kKW * 32, kKRows = 64;
+constexpr int kKPh = 4;                                  // tiles per phase
+constexpr int kKTileElems = kKRows * 64;                 // one 64 x 64 bf16 tile
 
 struct GkvArgs {
   const bf16_t* q;
   const bf16_t* dco;
   const bf16_t* ks;
   const bf16_t* vs;
-  const float* lse;
-  const float* dd;
+  const float* nls;        // -lse * log2(e) of the compressed branch [N, Hq]
+  const float* ndd;        // -D of the compressed branch [N, Hq]
   const int32_t* c2p;
   float* dk;               // partials [nsplit, Hkv, M, 64]
   float* dv;
@@ -343,11 +353,35 @@ struct GkvArgs {
   int64_t cps;             // cells per slice
 };
 
+// Separate LDS arrays hold the two phases, so the compiler can tell the
+// copies in flight from the tiles being read: q and dO rows of the phase's
+// tiles, then per tile the 64 values of -lse*log2(e) and of -D.
+template <int I>
+struct KvBuf {
+  __device__ static __forceinline__ bf16_t* q() {
+    __shared__ __attribute__((aligned(16))) bf16_t b[kKPh * kKTileElems];
+    return b;
+  }
+  __device__ static __forceinline__ bf16_t* d() {
+    __shared__ __attribute__((aligned(16))) bf16_t b[kKPh * kKTileElems];
+    return b;
+  }
+  __device__ static __forceinline__ float* ld() {
+    __shared__ __attribute__((aligned(16))) float b[kKPh * 2 * kKRows];
+    return b;
+  }
+};
+
+// What a row past the slice reads: zero q and dO, -lse*log2(e) = -inf (so
+// p = 0) and -D = 0.
+struct __attribute__((aligned(16))) KvPad {
+  float zero[32];
+  float ninf;
+  float zero1[3];
+};
+__device__ KvPad g_kv_pad = {{}, -__builtin_inff(), {}};
+
 __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
-  __shared__ __attribute__((aligned(16))) bf16_t q_l[2][kKRows * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t d_l[2][kKRows * 64];
-  __shared__ __attribute__((aligned(16))) float ls_l[2][kKRows];
-  __shared__ __attribute__((aligned(16))) float dd_l[2][kKRows];
   const int64_t bid = blockIdx.x;
   const int split = (int)(bid % A.nsplit);
   const int grp = (int)((bid / A.nsplit) % A.hkv);
@@ -365,62 +399,70 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
   const int64_t c1 = c0 + A.cps < A.ncell ? c0 + A.cps : A.ncell;
   const int cpt = kKRows / A.grp;                    // cells per tile
   const int64_t nt = c1 > c0 ? (c1 - c0 + cpt - 1) / cpt : 0;
-  // staging: thread = (row, 16-byte chunk); chunk-0 threads also store the
-  // row's lse and D (rows past the slice get lse = +inf: p = 0).  Two tiles
-  // are in flight in registers: a tile's rows are loaded two tiles before
-  // they are stored to LDS, and their packed positions one tile before that.
-  const int srow = tid >> 3, sch = tid & 7;
-  const int head = grp * A.grp + srow % A.grp;
-  struct Stage {
-    u32x4 q, d;
-    float l, dd;
-    bool ok;
-  };
-  Stage sg0, sg1;
-  // every step issues the same loads (clamped addresses, results selected
-  // afterwards), so the memory-counter waits stay exact across the loop
-  // A position is the raw table entry plus a validity flag computed from the
-  // cell index alone, so nothing waits for the entry until the rows are due.
+  const int64_t nph = (nt + kKPh - 1) / kKPh;
+  const int head0 = grp * A.grp;
+
+  // Copy assignment.  Rows: copy i of a wave moves 8 rows of tile i (row
+  // 8*wave + lane/8, 16-byte chunk lane%8 of its LDS row; the tile swizzle is
+  // applied on the source side).  -lse*log2(e) / -D: wave w moves the 64
+  // values of array w%2 of tile w/2.  A position is the raw table entry plus a
+  // validity flag computed from the cell index alone, so nothing waits for
+  // the entry until the copies that use it are issued, a phase later.
+  const int crow = wave * 8 + (lane >> 3);
+  const int cch = (lane & 7) ^ ((((crow >> 1) & 1) << 2) | ((crow >> 2) & 3));
+  const int chead = head0 + crow % A.grp;
+  const int lhead = head0 + lane % A.grp;
   struct Pos {
-    int32_t p;
-    bool ok;
+    int32_t p[kKPh];
+    bool ok[kKPh];
+    int32_t lp;
+    bool lok;
   };
-  auto position = [&](int64_t t) -> Pos {
-    const int64_t cell = c0 + t * cpt + srow / A.grp;
-    return Pos{A.c2p[cell < c1 ? cell : c1 - 1], cell < c1};
+  auto position = [&](int64_t c) -> int32_t { return A.c2p[c < c1 ? c : c1 - 1]; };
+  auto positions = [&](int64_t ph, Pos& P) {
+#pragma unroll
+    for (int i = 0; i < kKPh; ++i) {
+      const int64_t cell = c0 + (ph * kKPh + i) * cpt + crow / A.grp;
+      P.p[i] = position(cell);
+      P.ok[i] = cell < c1;
+    }
+    const int64_t cell = c0 + (ph * kKPh + (wave >> 1)) * cpt + lane / A.grp;
+    P.lp = position(cell);
+    P.lok = cell < c1;
   };
-  auto load = [&](Stage& sg, Pos pos) {
-    sg.ok = pos.ok;
-    const int64_t r = (int64_t)(pos.ok ? pos.p : 0) * A.hq + head;
-    sg.q = ld16(A.q + r * 64 + sch * 8);
-    sg.d = ld16(A.dco + r * 64 + sch * 8);
-    sg.l = A.lse[r];
-    sg.dd = A.dd[r];
+  auto issue = [&](bf16_t* bq, bf16_t* bd, float* bl, const Pos& P) {
+#pragma unroll
+    for (int i = 0; i < kKPh; ++i) {
+      const int64_t r = (int64_t)P.p[i] * A.hq + chead;
+      const void* sq = P.ok[i] ? (const void*)(A.q + r * 64 + cch * 8) : (const void*)g_kv_pad.zero;
+      const void* sd = P.ok[i] ? (const void*)(A.dco + r * 64 + cch * 8) : (const void*)g_kv_pad.zero;
+      __builtin_amdgcn_global_load_lds(sq, (lb::lds_ptr)(bq + i * kKTileElems + wave * 512), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds(sd, (lb::lds_ptr)(bd + i * kKTileElems + wave * 512), 16, 0,
+                                       0);
+    }
+    const int64_t r = (int64_t)P.lp * A.hq + lhead;
+    const float* src = (wave & 1) ? A.ndd : A.nls;
+    const void* sl = P.lok ? (const void*)(src + r)
+                           : (const void*)((wave & 1) ? g_kv_pad.zero1 : &g_kv_pad.ninf);
+    __builtin_amdgcn_global_load_lds(sl, (lb::lds_ptr)(bl + wave * 64), 4, 0, 0);
   };
-  auto store = [&](const Stage& sg, int b) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    st16(q_l[b] + TL::chunk_off(srow, sch), sg.ok ? sg.q : z);
-    st16(d_l[b] + TL::chunk_off(srow, sch), sg.ok ? sg.d : z);
-    // the row's 8 threads write the same values: -lse (log2 units) and -D,
-    // the starting values of the S and dP accumulators
-    ls_l[b][srow] = sg.ok ? -(sg.l * kLog2e) : -__builtin_inff();
-    dd_l[b][srow] = sg.ok ? -sg.dd : 0.0f;
-  };
-  auto tile = [&](int b) {
+  auto tile = [&](const bf16_t* q_l, const bf16_t* d_l, const float* ls_l) {
+    const float* dd_l = ls_l + kKRows;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       bf16x8 qr[4], dr[4];
-      row_frags(q_l[b], rb * 32 + col, h, qr);
-      row_frags(d_l[b], rb * 32 + col, h, dr);
+      row_frags(q_l, rb * 32 + col, h, qr);
+      row_frags(d_l, rb * 32 + col, h, dr);
       // accumulator element v holds query row rb*32 + 8*(v/4) + 4h + v%4:
-      // start S at -lse and dP at -D, so the products come out as the
-      // exponent of p and as dP - D
+      // start S at -lse (log2 units) and dP at -D, so the products come out
+      // as the exponent of p and as dP - D
       f32x16 nl, nd;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int r0 = rb * 32 + 8 * q4 + 4 * h;
-        const f32x4 L = *reinterpret_cast<const f32x4*>(&ls_l[b][r0]);
-        const f32x4 D = *reinterpret_cast<const f32x4*>(&dd_l[b][r0]);
+        const f32x4 L = *reinterpret_cast<const f32x4*>(&ls_l[r0]);
+        const f32x4 D = *reinterpret_cast<const f32x4*>(&dd_l[r0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           nl[4 * q4 + j] = L[j];
@@ -444,8 +486,8 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         bf16x8 dt[2], qt[2];
-        tr_frags(d_l[b], rb * 32, db, lane, dt);
-        tr_frags(q_l[b], rb * 32, db, lane, qt);
+        tr_frags(d_l, rb * 32, db, lane, dt);
+        tr_frags(q_l, rb * 32, db, lane, qt);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           dv[db] = Mma<bf16_t>::mma(dt[tt], pf[tt], dv[db]);
@@ -454,37 +496,26 @@ __global__ __launch_bounds__(64 * kKW) void k_glob_dkv(GkvArgs A) {
       }
     }
   };
-  // One step: publish tile t (held in sg), then refill sg with tile t + 2.
-  // Positions run one tile ahead of the rows and are issued before them, so
-  // waiting for a position never waits for the rows loaded after it.  The
-  // stream is padded to an even number of tiles (a padding tile has no rows:
-  // p = 0, adding exact zeros).
-  Pos pnext;
-  auto step = [&](Stage& sg, int64_t t) {
-    const int b = (int)(t & 1);
-    store(sg, b);
+  // The stream is padded to whole phases: a padding tile has no rows (p = 0,
+  // adding exact zeros).
+  auto phase = [&](auto cur, auto nxt, int64_t ph, const Pos& pn, Pos& pf) {
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    const Pos pn = position(t + 3);
-    load(sg, pnext);
-    pnext = pn;
-    __builtin_amdgcn_sched_barrier(0);
-    tile(b);
-    __builtin_amdgcn_sched_barrier(0);
+    if (ph + 1 < nph) issue(decltype(nxt)::q(), decltype(nxt)::d(), decltype(nxt)::ld(), pn);
+    if (ph + 2 < nph) positions(ph + 2, pf);
+#pragma unroll
+    for (int i = 0; i < kKPh; ++i)
+      tile(decltype(cur)::q() + i * kKTileElems, decltype(cur)::d() + i * kKTileElems,
+           decltype(cur)::ld() + i * 2 * kKRows);
   };
-  if (nt > 0) {
-    // the same issue order as a step: position, then the rows
-    const Pos p0 = position(0), p1 = position(1);
-    __builtin_amdgcn_sched_barrier(0);
-    load(sg0, p0);
-    __builtin_amdgcn_sched_barrier(0);
-    pnext = position(2);
-    __builtin_amdgcn_sched_barrier(0);
-    load(sg1, p1);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int64_t t = 0; t < nt; t += 2) {
-      step(sg0, t);
-      step(sg1, t + 1);
+  if (nph > 0) {
+    Pos pa, pb;
+    positions(0, pa);
+    issue(KvBuf<0>::q(), KvBuf<0>::d(), KvBuf<0>::ld(), pa);
+    if (nph > 1) positions(1, pb);
+    for (int64_t ph = 0; ph < nph; ph += 2) {
+      phase(KvBuf<0>{}, KvBuf<1>{}, ph, pb, pa);
+      if (ph + 1 < nph) phase(KvBuf<1>{}, KvBuf<0>{}, ph + 1, pa, pb);
     }
   }
   if (!kok) return;
@@ -1045,8 +1076,9 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
   hipError_t e;
   // 1. per-token prep
   hipLaunchKernelGGL(bw::k_bwd_prep, dim3((unsigned)((g.N + 3) / 4)), dim3(256), 0, s,
-                     (const bf16_t*)b.dout, b.o_loc, b.o_cmp, b.gate, g.N, g.Hq,
-                     g.gate_per_head, (bf16_t*)b.dlo, (bf16_t*)b.dco, b.d_loc, b.d_cmp, b.dgate);
+                     (const bf16_t*)b.dout, b.o_loc, b.o_cmp, b.gate, b.lse_cmp, g.N, g.Hq,
+                     g.gate_per_head, (bf16_t*)b.dlo, (bf16_t*)b.dco, b.d_loc, b.d_cmp, b.nls_cmp,
+                     b.dgate);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 2. local dq (first writer of dq_acc), 3. summary dq (adds)
   switch (g.G) {
@@ -1072,7 +1104,7 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
     A.ks = (const bf16_t*)b.k_sum;
     A.vs = (const bf16_t*)b.v_sum;
     A.lse = b.lse_cmp;
-    A.dd = b.d_cmp;
+    A.ndd = b.d_cmp;
     A.dq = b.dq_acc;
     A.m = g.M;
     A.n = g.N;
@@ -1143,8 +1175,8 @@ hipError_t launch_backward(const Geom& g, const BwdBuffers& b, hipStream_t s) {
     A.dco = (const bf16_t*)b.dco;
     A.ks = (const bf16_t*)b.k_sum;
     A.vs = (const bf16_t*)b.v_sum;
-    A.lse = b.lse_cmp;
-    A.dd = b.d_cmp;
+    A.nls = b.nls_cmp;
+    A.ndd = b.d_cmp;
     A.c2p = b.c2p;
     A.dk = b.dk_part;
     A.dv = b.dv_part;

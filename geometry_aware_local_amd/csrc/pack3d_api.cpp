@@ -177,7 +177,8 @@ SavedLayout saved_layout(const Geom& g) {
 }
 
 struct BwdLayout {
-  size_t q_rot, k_rot, k_sum, v_sum, dlo, dco, d_loc, d_cmp, dq_acc, dk_part, dv_part, total;
+  size_t q_rot, k_rot, k_sum, v_sum, dlo, dco, d_loc, d_cmp, nls_cmp, dq_acc, dk_part, dv_part,
+      total;
 };
 
 BwdLayout bwd_layout(const Geom& g) {
@@ -196,6 +197,7 @@ BwdLayout bwd_layout(const Geom& g) {
   take(w.dco, (size_t)g.N * g.Hq * 64 * 2);
   take(w.d_loc, (size_t)g.N * g.Hq * 4);
   take(w.d_cmp, (size_t)g.N * g.Hq * 4);
+  take(w.nls_cmp, (size_t)g.N * g.Hq * 4);
   take(w.dq_acc, (size_t)g.N * g.Hq * 64 * 4);
   take(w.dk_part, nsplit * g.Hkv * g.M * 64 * 4);
   take(w.dv_part, nsplit * g.Hkv * g.M * 64 * 4);
@@ -619,6 +621,7 @@ int pack3d_backward(const pack3d_problem* prob, const void* q, const void* k_loc
   b.dco = ws + w.dco;
   b.d_loc = (float*)(ws + w.d_loc);
   b.d_cmp = (float*)(ws + w.d_cmp);
+  b.nls_cmp = (float*)(ws + w.nls_cmp);
   b.dq_acc = (float*)(ws + w.dq_acc);
   b.dk_part = (float*)(ws + w.dk_part);
   b.dv_part = (float*)(ws + w.dv_part);

@@ -131,8 +131,9 @@ struct BwdBuffers {
   const void* v_sum;
   void* dlo;                   // workspace: g_loc * dO, g_cmp * dO (bf16)
   void* dco;
-  float* d_loc;                // workspace: D of each branch [N, Hq]
-  float* d_cmp;
+  float* d_loc;                // workspace: D of the local branch [N, Hq]
+  float* d_cmp;                //   and -D of the compressed branch
+  float* nls_cmp;              // workspace: -lse_cmp * log2(e) [N, Hq]
   float* dq_acc;               // workspace: rotated-frame dq [N, Hq, 64]
   float* dk_part;              // workspace: summary gradient partials
   float* dv_part;              //   [splits, Hkv, M, 64]
