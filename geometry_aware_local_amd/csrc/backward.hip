@@ -597,9 +597,9 @@ __global__ __launch_bounds__(64 * lb::Cfg<G>::W) void k_loc_dq(LdqArgs A) {
         const int cell = pc * 8 + (lane >> 3), cp = lane & 7;
         const int64_t row = (int64_t)pos[i] * rstride;
         __builtin_amdgcn_global_load_lds(
-            (const void*)(kg + row + k_swz(cell / RX, cell % RX, cp) * 8),
+            (const void*)(kg + row + kv_swz(cell / RX, cell % RX, cp) * 8),
             (lds_ptr)(kl + pc * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vg + row + v_swz(cell, cp) * 8),
+        __builtin_amdgcn_global_load_lds((const void*)(vg + row + kv_swz(cell / RX, cell % RX, cp) * 8),
                                          (lds_ptr)(vl + pc * 512), 16, 0, 0);
       }
     }
@@ -633,8 +633,8 @@ __global__ __launch_bounds__(64 * lb::Cfg<G>::W) void k_loc_dq(LdqArgs A) {
   int koff[4], voff[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    koff[st] = kcell * 64 + k_swz(ky0, kx0, h * 4 + st) * 8;
-    voff[st] = kcell * 64 + v_swz(kcell, h * 4 + st) * 8;
+    koff[st] = kcell * 64 + kv_swz(ky0, kx0, h * 4 + st) * 8;
+    voff[st] = kcell * 64 + kv_swz(ky0, kx0, h * 4 + st) * 8;
   }
   const int r4 = lane & 15;
   int toff[2][2];   // [half][db]: K^T rows, + (4kb + 2t) region rows per step
@@ -644,7 +644,7 @@ __global__ __launch_bounds__(64 * lb::Cfg<G>::W) void k_loc_dq(LdqArgs A) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int dim = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (r4 & 3);
-      toff[half][db] = cell * 64 + k_swz(ty_, tx_, dim >> 3) * 8 + (dim & 7);
+      toff[half][db] = cell * 64 + kv_swz(ty_, tx_, dim >> 3) * 8 + (dim & 7);
     }
   }
 
@@ -748,9 +748,14 @@ constexpr int kDBlk = kDSY * kDRX / 32;  // 32-slot blocks per wave (5)
 static_assert(kDSY * kDRX % 32 == 0, "whole slot blocks");
 static_assert(kDRC % 8 == 0, "1 KB pieces");
 
-// chunk position in a region cell's row: 16 lanes read 16 consecutive
-// columns of one region row (bank half = column parity)
-__device__ __forceinline__ int q_swz(int cell, int chunk) { return chunk ^ ((cell >> 1) & 7); }
+// chunk position in a region cell's row (cells numbered row-major, 16 per
+// region row).  Row reads take 16 consecutive cells per 16 lanes, the
+// transposing reads 4 consecutive cells x 4 aligned chunks per 32 lanes; the
+// tile swizzle 4 ((cell >> 1) & 1) + ((cell >> 2) & 3) serves both without
+// bank conflicts (cells c and c + 2 land in different 4-chunk halves).
+__device__ __forceinline__ int q_swz(int cell, int chunk) {
+  return chunk ^ ((((cell >> 1) & 1) << 2) | ((cell >> 2) & 3));
+}
 
 struct LkvArgs {
   const bf16_t* q;         // rotated queries

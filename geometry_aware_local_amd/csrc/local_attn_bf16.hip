@@ -103,9 +103,9 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
       if (pc < RCP / 8) {
         const int cell = pc * 8 + (lane >> 3), cp = lane & 7;
         const int64_t row = (int64_t)pos[i] * rstride;
-        __builtin_amdgcn_global_load_lds((const void*)(kg + row + k_swz(cell / RX, cell % RX, cp) * 8),
+        __builtin_amdgcn_global_load_lds((const void*)(kg + row + kv_swz(cell / RX, cell % RX, cp) * 8),
                                          (lds_ptr)(kl + pc * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vg + row + v_swz(cell, cp) * 8),
+        __builtin_amdgcn_global_load_lds((const void*)(vg + row + kv_swz(cell / RX, cell % RX, cp) * 8),
                                          (lds_ptr)(vl + pc * 512), 16, 0, 0);
       }
     }
@@ -147,16 +147,16 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_bf16(Args A) {
   const int ky0 = py0 + col / 8, kx0 = px0 + col % 8, kcell = ky0 * RX + kx0;
   int koff[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) koff[st] = kcell * 64 + k_swz(ky0, kx0, h * 4 + st) * 8;
+  for (int st = 0; st < 4; ++st) koff[st] = kcell * 64 + kv_swz(ky0, kx0, h * 4 + st) * 8;
   const int r4 = lane & 15;
   int voff[2][2];   // [half][dim block]; + (4*kb + 2t)*RX cells per PV step
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int cell = (py0 + half) * RX + px0 + 4 * h + (r4 >> 2);
+    const int vy = py0 + half, vx = px0 + 4 * h + (r4 >> 2), cell = vy * RX + vx;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int dim = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (r4 & 3);
-      voff[half][db] = cell * 64 + v_swz(cell, dim >> 3) * 8 + (dim & 7);
+      voff[half][db] = cell * 64 + kv_swz(vy, vx, dim >> 3) * 8 + (dim & 7);
     }
   }
 
@@ -356,10 +356,10 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
       if (pc < RCP / 8) {
         const int cell = pc * 8 + (lane >> 3), cp = lane & 7;
         const int64_t row = (int64_t)pos[i] * rstride;
-        __builtin_amdgcn_global_load_lds((const void*)(kg + row + k_swz(cell / RX, cell % RX, cp) * 8),
+        __builtin_amdgcn_global_load_lds((const void*)(kg + row + kv_swz(cell / RX, cell % RX, cp) * 8),
                                          (lds_ptr)(kl + pc * 512), 16, 0, 0);
         if (cell < RC)
-          __builtin_amdgcn_global_load_lds((const void*)(vg + row + v_swz(cell, cp) * 8),
+          __builtin_amdgcn_global_load_lds((const void*)(vg + row + kv_swz(cell / RX, cell % RX, cp) * 8),
                                            (lds_ptr)(vl + pc * 512), 16, 0, 0);
       }
     }
@@ -391,16 +391,16 @@ __global__ __launch_bounds__(64 * Cfg<G>::W) void k_local_zrun(Args A) {
   const int ky0 = py0 + col / 8, kx0 = px0 + col % 8, kcell = ky0 * RX + kx0;
   int koff[4];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) koff[st] = kcell * 64 + k_swz(ky0, kx0, h * 4 + st) * 8;
+  for (int st = 0; st < 4; ++st) koff[st] = kcell * 64 + kv_swz(ky0, kx0, h * 4 + st) * 8;
   const int r4 = lane & 15;
   int voff[2][2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int cell = (py0 + half) * RX + px0 + 4 * h + (r4 >> 2);
+    const int vy = py0 + half, vx = px0 + 4 * h + (r4 >> 2), cell = vy * RX + vx;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int dim = db * 32 + 16 * ((lane >> 4) & 1) + 4 * (r4 & 3);
-      voff[half][db] = cell * 64 + v_swz(cell, dim >> 3) * 8 + (dim & 7);
+      voff[half][db] = cell * 64 + kv_swz(vy, vx, dim >> 3) * 8 + (dim & 7);
     }
   }
 

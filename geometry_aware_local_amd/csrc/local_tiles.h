@@ -37,17 +37,22 @@ struct Cfg {
   static_assert(RX % 2 == 0, "a cell's bank half is the parity of its column");
 };
 
-// 16-byte chunk positions in a cell's 128-byte LDS row.  gfx950 LDS has 64
-// four-byte banks and serves a 128-bit read 16 lanes at a time; a cell
-// (y, x) of the region sits in bank half x & 1 (RX is even).  A K operand
-// read takes 8 consecutive columns of 2 consecutive region rows per 16
-// lanes, so the position depends on (x >> 1) and on the row parity: all 16
-// (half, position) pairs differ.  V: the transposing read takes 4
-// consecutive cells x 16 dims per 16 lanes.
-__device__ __forceinline__ int k_swz(int y, int x, int chunk) {
-  return chunk ^ (((x >> 1) + 4 * (y & 1)) & 7);
+// 16-byte chunk positions in a cell's 128-byte LDS row, for the K and the V
+// tiles alike (both are read as rows and, in the backward, transposed).
+// gfx950 LDS has 64 four-byte banks; it serves a 128-bit read 16 lanes at a
+// time and the 8-byte transposing read 32 lanes at a time.  A cell (y, x) of
+// the region sits in bank half x & 1 (RX is even).  A row read takes 8
+// consecutive columns of 2 consecutive region rows per 16 lanes: within a
+// bank half, 4 consecutive values of x >> 1 times 2 row parities need
+// distinct positions.  A transposing read takes 4 consecutive cells of one
+// region row times 4 aligned chunks per 32 lanes: the cells x and x + 2 (one
+// bank half) need their chunks in different 4-chunk halves.
+// sw = 4 ((x >> 1) & 1) + ((x >> 2) & 1) + 2 (y & 1) does both: 4
+// consecutive x >> 1 give distinct (bit 0, bit 1) pairs, and x + 2 flips
+// bit 0 of x >> 1, hence bit 2 of sw.
+__device__ __forceinline__ int kv_swz(int y, int x, int chunk) {
+  return chunk ^ (4 * ((x >> 1) & 1) + ((x >> 2) & 1) + 2 * (y & 1));
 }
-__device__ __forceinline__ int v_swz(int cell, int chunk) { return chunk ^ ((2 * cell) & 6); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
