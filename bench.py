@@ -45,14 +45,19 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 METRIC = "PACK3D attention fwd tokens/sec at 262k tokens; % bf16 MFMA peak; HBM GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_global_attn_block_bf16_64x64x64_hbm_traffic.txt")
 GLOBAL_SOURCES = [os.path.join(ROOT, "geometry_aware_local_amd", "csrc", f)
-                  for f in ("global_attn.hip", "pack3d_device.h")] + [
-                  os.path.join(ROOT, "geometry_aware_local_amd", "build.py")]
+                  for f in ("global_attn.hip", "pack3d_device.h", "local_tiles.h")]
 
 
 def source_sha(paths) -> str:
+    """Hash of the compressed kernel's sources and of the compiler flags its
+    file is built with (the counters belong to that build only)."""
+    from geometry_aware_local_amd import build as gb
     h = hashlib.sha256()
     for p in paths:
         h.update(open(p, "rb").read())
+    flags = [f for f in gb.FLAGS + gb.FILE_FLAGS.get("global_attn.hip", [])
+             if f != "-I" and not os.path.isabs(f)]     # include paths vary by checkout
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

@@ -37,6 +37,10 @@ FLAGS = [
 FILE_FLAGS = {
     "global_attn.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "layer.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    # MFMA results in VGPRs: the local dk/dv kernel (one wave per SIMD, so
+    # 512 registers available) otherwise keeps its S and dP accumulators in
+    # AGPRs and copies every element back before the exponentials
+    "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
