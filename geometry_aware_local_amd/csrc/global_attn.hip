@@ -193,12 +193,67 @@ __device__ __forceinline__ bf16x8 rowsum_ones(int lane) {
 }
 
 // One 64-key tile for all of the wave's column blocks.
-template <typename T, int CB, int MODE>
+template <typename T, int CB, int MODE, bool kFull = false>
 __device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __restrict__ vl,
                                        int k0, int m,
                                        float c, const QFrag<T> (&qf)[CB], GCol (&st)[CB],
                                        f32x16 (&o)[CB][2], int lane, const bf16x8& ones) {
   const int h = lane >> 5, col = lane & 31;
+  if constexpr (MODE != kGeneral) {
+    // no tile maximum needed: each 32-key half runs logits -> exponentials
+    // -> PV on its own (half the live logits and probabilities)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sk[CB];
+      {
+        KFrag<T> kf;
+        load_kfrag<T>(kf, kl, kb * 32 + col, h);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) sk[cb] = qk_tile<T>(kf, qf[cb]);
+      }
+      if (!kFull && k0 + kGKt > m) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = k0 + kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (key >= m)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) sk[cb][v] = kNegInf;
+        }
+      }
+      typename Mma<T>::frag pk[CB][Mma<T>::kPvSteps];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float mu = st[cb].m == kNegInf ? 0.0f : st[cb].m;
+        f32x16 p;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if constexpr (MODE == kZeroRef)
+            p[v] = __builtin_amdgcn_exp2f(sk[cb][v]);
+          else
+            p[v] = __builtin_amdgcn_exp2f(fmaf(sk[cb][v], c, -mu));
+        }
+#pragma unroll
+        for (int t = 0; t < Mma<T>::kPvSteps; ++t) {
+          pk[cb][t] = Mma<T>::p_frag(p, t);
+          if constexpr (GLds<T>::kF32)
+            st[cb].l = frag_sum(pk[cb][t], st[cb].l);
+          else
+            st[cb].lm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[cb][t], st[cb].lm,
+                                                                0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        typename Mma<T>::frag vf[Mma<T>::kPvSteps];
+        v_frags<T>(vf, vl, db, kb * 32, lane);
+#pragma unroll
+        for (int t = 0; t < Mma<T>::kPvSteps; ++t)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) o[cb][db] = Mma<T>::mma(vf[t], pk[cb][t], o[cb][db]);
+      }
+    }
+    return;
+  }
   f32x16 s[2][CB];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -207,7 +262,7 @@ __device__ __forceinline__ void g_tile(const T* __restrict__ kl, const T* __rest
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) s[kb][cb] = qk_tile<T>(kf, qf[cb]);
   }
-  if (k0 + kGKt > m) {
+  if (!kFull && k0 + kGKt > m) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -345,6 +400,10 @@ __device__ __forceinline__ void g_stream_ph(const bf16_t* ksg, const bf16_t* vsg
   const int nt = (m + kGKt - 1) / kGKt;
   const int nph = (nt + kPhR - 1) / kPhR;
   const bf16x8 ones = rowsum_ones(lane);
+  // full tiles run without the key mask; a ragged last tile runs once after
+  // the stream, from its phase's buffer (nothing overwrites it after the
+  // last phase's barrier)
+  const int ntf = m / kGKt;
   auto phase = [&](int ph, bf16_t* __restrict__ cur, bf16_t* __restrict__ nxt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -352,14 +411,20 @@ __device__ __forceinline__ void g_stream_ph(const bf16_t* ksg, const bf16_t* vsg
 #pragma unroll
     for (int i = 0; i < kPhR; ++i) {
       const int t = ph * kPhR + i;
-      if (t < nt)
-        g_tile<bf16_t, CB, MODE>(cur + i * kPhTile, cur + i * kPhTile + kGKt * 64, t * kGKt, m,
-                                 A.c, qf, st, o, lane, ones);
+      if (t < ntf)
+        g_tile<bf16_t, CB, MODE, true>(cur + i * kPhTile, cur + i * kPhTile + kGKt * 64,
+                                       t * kGKt, m, A.c, qf, st, o, lane, ones);
     }
   };
   for (int ph = 0; ph < nph; ph += 2) {
     phase(ph, ph_buf<0>(), ph_buf<1>());
     if (ph + 1 < nph) phase(ph + 1, ph_buf<1>(), ph_buf<0>());
+  }
+  if (ntf < nt) {
+    const int t = nt - 1, i = t % kPhR;
+    bf16_t* buf = ((t / kPhR) & 1) ? ph_buf<1>() : ph_buf<0>();
+    g_tile<bf16_t, CB, MODE, false>(buf + i * kPhTile, buf + i * kPhTile + kGKt * 64, t * kGKt, m,
+                                    A.c, qf, st, o, lane, ones);
   }
 }
 
