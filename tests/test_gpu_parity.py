@@ -408,22 +408,21 @@ def test_forward_1m_random_sampled(pk):
 
 def test_dense_companion_1m_sampled(pk):
     """The dense axial-RoPE attention the bench times beside the forward at
-    1 048 576 tokens: 1x1x1 blocks with a = 1 make the compressed branch
-    attend to every rotated key (m = N), checked on sampled rows against the
-    oracle's dense softmax over all N keys."""
+    1 048 576 tokens: the forward with 1x1x1 blocks and a = 1, whose
+    compressed branch attends to every rotated key (m = N).  The gate logits
+    (-40, +40) select that branch (g_loc = e^-80), so sampled output rows are
+    checked against the oracle's dense softmax over all N keys."""
     w = RANDOM
     _say("dense companion", w.name)
     inp = sg.make_inputs(w)
     d = gu.device_inputs(inp)
-    prob = gu.problem(pk, w)
     dprob = gu.problem(pk, w.with_(block=(1, 1, 1)))
-    q_rot = pk.pack3d_rope(prob, d["q"], d["coords"])
-    dk, dv = pk.pack3d_block_summary(dprob, d["k_cmp"], d["v_cmp"], None, d["cell_to_pos"])
-    assert dk.shape[1] == w.n_tokens
-    o = pk.pack3d_global_attn(dprob, q_rot, dk, dv)
+    gate = torch.tensor([-40.0, 40.0], dtype=torch.float32).repeat(w.n_tokens, 1).cuda()
+    out = pk.pack3d_forward(dprob, d["q"], d["k_loc"], d["v_loc"], d["k_cmp"], d["v_cmp"], None,
+                            d["coords"], d["cell_to_pos"], gate)
     rows = _rows(w, 48, seed=6)
-    got = gu.host(o[torch.from_numpy(rows).cuda()])
-    del o, dk, dv, q_rot, d
+    got = gu.host(out[torch.from_numpy(rows).cuda()])
+    del out, d, gate
     torch.cuda.empty_cache()
     qr = orc.rotate(inp.q[rows], inp.coords[rows])
     rk, rv = orc.block_summaries(inp.k_cmp, inp.v_cmp, None, inp.coords, w.grid, (1, 1, 1))
