@@ -781,6 +781,7 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
   __shared__ __attribute__((aligned(16))) bf16_t d_l[kDRC * 64];
   __shared__ __attribute__((aligned(16))) float ls_l[kDRC];
   __shared__ __attribute__((aligned(16))) float dd_l[kDRC];
+  __shared__ int32_t pos_l[2][kDRC];
   const int64_t bid = blockIdx.x;
   const int64_t lin = (bid % kNumXcd) * A.per_xcd + bid / kNumXcd;
   if (lin >= A.nblocks) return;
@@ -837,16 +838,36 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
   const int zlo = z0 - A.rz < 0 ? 0 : z0 - A.rz;
   const int zhi = z0 + A.rz >= A.Z ? A.Z - 1 : z0 + A.rz;
   constexpr int kPieces = kDRC / 8;
+  // Packed positions of the region's cells in the current plane (-1: off the
+  // lattice) sit in LDS, read once per plane: the next plane's load during
+  // the current plane's last head and are stored after its compute, so each
+  // plane-and-head step waits for one round of loads (rows, lse, D) only.
+  constexpr int kPosPer = (kDRC + 64 * kDW - 1) / (64 * kDW);
+  auto region_pos = [&](int zz, int cell) -> int32_t {
+    const int yy = y0 - lb::kHalo + cell / kDRX, xx = x0 - lb::kHalo + cell % kDRX;
+    const bool ok = cell < kDRC && yy >= 0 && yy < A.Y && xx >= 0 && xx < A.X;
+    return ok ? A.c2p[((int64_t)zz * A.Y + yy) * A.X + xx] : -1;
+  };
+  {
+    int32_t p0[kPosPer];
+#pragma unroll
+    for (int k = 0; k < kPosPer; ++k) p0[k] = region_pos(zlo, tid + 64 * kDW * k);
+#pragma unroll
+    for (int k = 0; k < kPosPer; ++k)
+      if (tid + 64 * kDW * k < kDRC) pos_l[0][tid + 64 * kDW * k] = p0[k];
+  }
+  __syncthreads();
+  int pb = 0;
   for (int zz = zlo; zz <= zhi; ++zz) {
     for (int hd = 0; hd < A.G; ++hd) {
       const int head = grp * A.G + hd;
+      const int32_t* pos = pos_l[pb];
       // copies of the region's q and g_loc*dO rows for this plane and head
+      // (cells off the lattice copy row 0: finite, and masked to p = 0)
       for (int pc = wave; pc < kPieces; pc += kDW) {
         const int cell = pc * 8 + (lane >> 3), cp = lane & 7;
-        const int yy = y0 - lb::kHalo + cell / kDRX, xx = x0 - lb::kHalo + cell % kDRX;
-        const bool ok = yy >= 0 && yy < A.Y && xx >= 0 && xx < A.X;
-        const int64_t r = ok ? (int64_t)A.c2p[((int64_t)zz * A.Y + yy) * A.X + xx] * A.hq + head
-                             : head;
+        const int32_t pp = pos[cell];
+        const int64_t r = (int64_t)(pp >= 0 ? pp : 0) * A.hq + head;
         const int src = q_swz(cell, cp);
         __builtin_amdgcn_global_load_lds((const void*)(A.q + r * 64 + src * 8),
                                          (lb::lds_ptr)(q_l + pc * 512), 16, 0, 0);
@@ -854,11 +875,10 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
                                          (lb::lds_ptr)(d_l + pc * 512), 16, 0, 0);
       }
       for (int cell = tid; cell < kDRC; cell += 64 * kDW) {
-        const int yy = y0 - lb::kHalo + cell / kDRX, xx = x0 - lb::kHalo + cell % kDRX;
-        const bool ok = yy >= 0 && yy < A.Y && xx >= 0 && xx < A.X;
+        const int32_t pp = pos[cell];
         float l = __builtin_inff(), d = 0.0f;   // off the lattice: p = 0
-        if (ok) {
-          const int64_t r = (int64_t)A.c2p[((int64_t)zz * A.Y + yy) * A.X + xx] * A.hq + head;
+        if (pp >= 0) {
+          const int64_t r = (int64_t)pp * A.hq + head;
           l = A.lse[r] * kLog2e;
           d = A.dd[r];
         }
@@ -867,6 +887,10 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      const bool next_plane = hd == A.G - 1 && zz < zhi;
+      int32_t np[kPosPer];
+#pragma unroll
+      for (int k = 0; k < kPosPer; ++k) np[k] = next_plane ? region_pos(zz + 1, tid + 64 * kDW * k) : -1;
 #pragma unroll
       for (int blk = 0; blk < kDBlk; ++blk) {
         const int boff = 2 * blk * kDRX * 64;    // two region rows per block
@@ -920,8 +944,14 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
           }
         }
       }
+      if (next_plane) {
+#pragma unroll
+        for (int k = 0; k < kPosPer; ++k)
+          if (tid + 64 * kDW * k < kDRC) pos_l[pb ^ 1][tid + 64 * kDW * k] = np[k];
+      }
       __syncthreads();
     }
+    pb ^= 1;
   }
 
   if (!kok) return;
