@@ -732,16 +732,19 @@ __global__ __launch_bounds__(64 * lb::Cfg<G>::W) void k_loc_dq(LdqArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// k_loc_dkv: workgroup = 2 waves = an 8 x 8 tile of key cells of one z-plane
-// and one KV group; wave w owns the 4 x 8 patch of rows 4w .. 4w+3 (its 32
-// key cells are the MFMA columns, held in registers).  The window is
-// symmetric, so a key's gradient sums over the queries in the box around
-// it: for every plane of the window and every head of the group the
-// workgroup copies the q and g_loc * dO rows of the 14 x 16 region (tile
-// plus a 3-cell halo, padded to 16 columns) into LDS, with lse and D per
-// cell; each wave contracts over its 10 x 16 query slots in 32-slot blocks.
+// k_loc_dkv: workgroup = 4 waves = an 8 x 8 tile of key cells of one z-plane
+// and one KV group; waves w and w + 2 own the 4 x 8 patch of rows
+// 4(w%2) .. 4(w%2)+3 (its 32 key cells are the MFMA columns, held in
+// registers).  The window is symmetric, so a key's gradient sums over the
+// queries in the box around it: for every plane of the window and every head
+// of the group the workgroup copies the q and g_loc * dO rows of the 14 x 16
+// region (tile plus a 3-cell halo, padded to 16 columns) into LDS, with lse
+// and D per cell.  A patch's 10 x 16 query slots form five 32-slot blocks;
+// its two waves split them 3 + 2 (which wave takes three alternates between
+// workgroups), so two workgroups share each SIMD and one computes while the
+// other waits for its copies; the two partial sums meet in LDS at the end.
 // ---------------------------------------------------------------------------
-constexpr int kDW = 2, kDTY = 8, kDTX = 8, kDRY = kDTY + 2 * lb::kHalo, kDRX = 16;
+constexpr int kDW = 4, kDTY = 8, kDTX = 8, kDRY = kDTY + 2 * lb::kHalo, kDRX = 16;
 constexpr int kDRC = kDRY * kDRX;      // 224 region cells
 constexpr int kDSY = 4 + 2 * lb::kHalo;  // query slot rows per wave (10)
 constexpr int kDBlk = kDSY * kDRX / 32;  // 32-slot blocks per wave (5)
@@ -792,7 +795,9 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
   const int y0 = ty * kDTY, x0 = tx * kDTX;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int py0 = 4 * wave;
+  const int kw = wave & 1, part = wave >> 1;
+  const int split = (lin & 1) ? 2 : 3;   // part 0: blocks < split, part 1: the rest
+  const int py0 = 4 * kw;
   const int ky = col / 8, kx = col % 8;
   const int yk = y0 + py0 + ky, xk = x0 + kx;
   const bool kok = yk < A.Y && xk < A.X;
@@ -893,6 +898,7 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
       for (int k = 0; k < kPosPer; ++k) np[k] = next_plane ? region_pos(zz + 1, tid + 64 * kDW * k) : -1;
 #pragma unroll
       for (int blk = 0; blk < kDBlk; ++blk) {
+        if ((blk < split) != (part == 0)) continue;
         const int boff = 2 * blk * kDRX * 64;    // two region rows per block
         bf16x8 qr[4], dr[4];
 #pragma unroll
@@ -954,7 +960,35 @@ __global__ __launch_bounds__(64 * kDW) void k_loc_dkv(LkvArgs A) {
     pb ^= 1;
   }
 
-  if (!kok) return;
+  // part 1 leaves its partial sums in the region buffers (free after the
+  // last step's barrier); part 0 adds them, always in this order
+  f32x4* red_k = reinterpret_cast<f32x4*>(q_l);
+  f32x4* red_v = reinterpret_cast<f32x4*>(d_l);
+  static_assert(2 * 2 * 4 * 64 * sizeof(f32x4) <= sizeof(q_l), "reduction fits");
+  if (part == 1) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int i = ((kw * 2 + db) * 4 + q4) * 64 + lane;
+        red_k[i] = f32x4{dk[db][4 * q4], dk[db][4 * q4 + 1], dk[db][4 * q4 + 2], dk[db][4 * q4 + 3]};
+        red_v[i] = f32x4{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]};
+      }
+  }
+  __syncthreads();
+  if (part == 1 || !kok) return;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int i = ((kw * 2 + db) * 4 + q4) * 64 + lane;
+      const f32x4 ek = red_k[i], ev = red_v[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dk[db][4 * q4 + j] += ek[j];
+        dv[db][4 * q4 + j] += ev[j];
+      }
+    }
   // dk_loc = R(c)^T (tau dk^R); pairs (2p, 2p+1) are adjacent elements
   const int kc[3] = {z0, yk, xk};
   bf16_t* ok_ = A.dk + krow * 64;
