@@ -37,9 +37,10 @@ FLAGS = [
 FILE_FLAGS = {
     "global_attn.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "layer.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-    # MFMA results in VGPRs: the local dk/dv kernel (one wave per SIMD, so
-    # 512 registers available) otherwise keeps its S and dP accumulators in
-    # AGPRs and copies every element back before the exponentials
+    # MFMA results in VGPRs: otherwise the local dk/dv kernel (whose launch
+    # bounds allow one wave per SIMD, hence AGPRs) keeps its S and dP
+    # accumulators in AGPRs and copies every element back before the
+    # exponentials; in VGPRs it fits two waves per SIMD
     "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
